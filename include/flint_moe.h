@@ -1,0 +1,168 @@
+/*
+ * flint_moe.h - C ABI of the MI355X (gfx950) Flint routed-expert MoE block.
+ *
+ * The block (vLLM page "vllm.models.flint.ops.moe", module docstring,
+ * "Numerics"; page "vllm.models.flint.model", FlintSparseMoeBlock):
+ *   logits = bf16(x @ router^T)                       (fp32 accumulation)
+ *   ids    = top_k experts by logit (ties -> lowest expert index)
+ *   s_j    = fp32 sigmoid of the selected logits (exact exp, RN division)
+ *   tw_j   = bf16(s_j / (sum_j s_j + 1e-20)), held in fp32
+ *   per pair (t, j), expert e = ids[t, j]:
+ *     g, u = fp32 (x[t] . W13[e, n]) * alpha13[e], (x[t] . W13[e, I + n]) * ...
+ *     act  = bf16(silu(g) * u)
+ *     y    = bf16((act . W2[e, h]) * alpha2[e])
+ *   routed = bf16(sum_j tw_j * y_j)                   (fp32 accumulation)
+ *   out    = bf16(routed + shared(x))                 (ungated shared SwiGLU)
+ * NVFP4 weights are E2M1 codes times one E4M3 scale per 16 consecutive K
+ * elements, dequantised exactly.  The shared expert and the BF16-expert
+ * variant use the same rounding points with bf16 weights and no alpha.
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers to row-major, densely packed arrays
+ *    owned by the caller.  bf16 tensors are passed as uint16_t bit patterns.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is queued
+ *    asynchronously; results are valid once the stream is synchronised.
+ *  - No entry point allocates or frees device memory, synchronises the
+ *    device, or keeps a pointer after its queued work completes.
+ *  - Inputs are never modified.  Outputs are fully overwritten.
+ *  - Arguments are validated on the host before anything is queued; a
+ *    non-zero status means nothing was queued (FLINT_ERR_HIP: a HIP launch
+ *    failed; flint_last_hip_error() gives its hipError_t).
+ *  - Device pointers must be 16-byte aligned (FLINT_ERR_ALIGN otherwise).
+ *  - Shapes: 1 <= top_k <= E <= 256; H % 256 == 0, 256 <= H <= 8192;
+ *    I % 128 == 0, 128 <= I <= 4096; SI (shared width) 0 or I-like.
+ *  - A workspace is used by one stream at a time: its counters are reset by
+ *    the kernels themselves, so launches using one workspace must be
+ *    serialised on one stream (as the pages require of their route counter).
+ */
+#ifndef FLINT_MOE_H
+#define FLINT_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum flint_status {
+  FLINT_OK = 0,
+  FLINT_ERR_NULL = -1,      /* a required pointer is NULL */
+  FLINT_ERR_SHAPE = -2,     /* unsupported or inconsistent sizes */
+  FLINT_ERR_ALIGN = -3,     /* a device pointer is not 16-byte aligned */
+  FLINT_ERR_WORKSPACE = -4, /* workspace missing or too small */
+  FLINT_ERR_HIP = -5        /* a HIP call failed */
+};
+
+/* NVFP4 routed experts in the ModelOpt checkpoint layout (page
+ * "vllm.models.flint.ops.moe", FlintMoEWeights.from_modelopt and
+ * FlintNvfp4Experts: w13 [E, 2I, H/2] with gate rows first, scales
+ * [E, 2I, H/16] float8_e4m3fn, one fp32 global scale per expert shared by
+ * gate and up; w2 [E, H, I/2], scales [E, H, I/16], fp32 [E]).
+ * Byte c of a row packs K elements 2c (low nibble) and 2c + 1 (high nibble). */
+typedef struct {
+  const uint8_t *w13; /* [E, 2I, H/2] E2M1 codes, rows 0..I-1 gate, I..2I-1 up */
+  const uint8_t *s13; /* [E, 2I, H/16] E4M3 block scales */
+  const float *a13;   /* [E] global scale of gate and up */
+  const uint8_t *w2;  /* [E, H, I/2] E2M1 codes */
+  const uint8_t *s2;  /* [E, H, I/16] E4M3 block scales */
+  const float *a2;    /* [E] global scale of down */
+} flint_nvfp4_experts;
+
+/* BF16 routed experts, plain row-major (the pages' BF16 decode path reads
+ * the same logical matrices through a TRTLLM block layout; page
+ * "vllm.models.flint.ops.moe", flint_moe_bf16_decode). */
+typedef struct {
+  const uint16_t *w13; /* [E, 2I, H] bf16, rows 0..I-1 gate, I..2I-1 up */
+  const uint16_t *w2;  /* [E, H, I] bf16 */
+} flint_bf16_experts;
+
+/* Ungated shared SwiGLU expert (page "vllm.models.flint.model": Flint has
+ * an ungated shared expert added to the routed sum).  w_gu == NULL means no
+ * shared expert (its output is taken as 0). */
+typedef struct {
+  const uint16_t *w_gu;   /* [2*SI, H] bf16, rows 0..SI-1 gate, SI..2SI-1 up */
+  const uint16_t *w_down; /* [H, SI] bf16 */
+  int SI;
+} flint_shared_expert;
+
+/* Optional inputs and outputs of the MoE entry points; NULL = unused.
+ * Intermediates use pair-major order p = t * top_k + j. */
+typedef struct {
+  const int32_t *ids_in; /* [M, top_k] forced routing (with tw_in): skips the router */
+  const float *tw_in;    /* [M, top_k] */
+  uint16_t *logits_out;  /* [M, E] bf16 router logits */
+  int32_t *ids_out;      /* [M, top_k] */
+  float *tw_out;         /* [M, top_k] */
+  uint16_t *act_out;     /* [M*top_k, I] bf16 */
+  uint16_t *y_out;       /* [M*top_k, H] bf16 */
+  uint16_t *sact_out;    /* [M, SI] bf16 shared-expert activations */
+  uint16_t *sh_out;      /* [M, H] bf16 shared-expert output */
+} flint_moe_debug;
+
+/* Status code -> static string. */
+const char *flint_status_str(int status);
+
+/* hipError_t of the last FLINT_ERR_HIP returned on the calling thread. */
+int flint_last_hip_error(void);
+
+/* Bytes of device workspace the MoE entry points need for these sizes
+ * (max_M tokens at most).  SI = 0 when there is no shared expert. */
+int flint_moe_workspace_bytes(int max_M, int H, int E, int I, int SI, int top_k,
+                              size_t *bytes);
+
+/* Zeroes a workspace (its counters must start at zero).  Call once after
+ * allocating it, on the stream that will use it. */
+int flint_moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
+/* Exact NVFP4 dequantisation (page "vllm.models.flint.ops.moe", _dequant8 /
+ * _dequant_rows: E2M1 value times E4M3 scale, exact in bf16): out[r, k] =
+ * bf16(e2m1(code(r, k)) * e4m3(s[r, k / 16])), no global scale.
+ * w [rows, K/2], s [rows, K/16], out [rows, K]; K % 32 == 0. */
+int flint_nvfp4_dequant(const uint8_t *w, const uint8_t *s, int rows, int K,
+                        uint16_t *out, void *stream);
+
+/* Top-k of bf16 logits (page "vllm.models.flint.ops.moe", _topk_kernel /
+ * _topk_row): ids [M, top_k] int32 in selection order, tw [M, top_k] fp32
+ * holding bf16 values; scores (may be NULL) [M, top_k] receives the fp32
+ * sigmoid scores s_j before renormalisation. */
+int flint_moe_topk(const uint16_t *logits, int M, int E, int top_k, int32_t *ids,
+                   float *tw, float *scores, void *stream);
+
+/* Router (page "vllm.models.flint.ops.moe", route / _router_kernel): bf16
+ * logits of x [M, H] against router [E, H], then top-k as flint_moe_topk.
+ * logits (may be NULL) [M, E].  Any M >= 1. */
+int flint_moe_route(const uint16_t *x, const uint16_t *router, int M, int H, int E,
+                    int top_k, uint16_t *logits, int32_t *ids, float *tw,
+                    void *ws, size_t ws_bytes, void *stream);
+
+/* The MoE block on NVFP4 experts for decode-size batches, 1 <= M <= 64
+ * (page "vllm.models.flint.ops.moe", flint_moe, decode branch):
+ * out [M, H] bf16. */
+int flint_moe_decode(const uint16_t *x, const uint16_t *router,
+                     const flint_nvfp4_experts *w, const flint_shared_expert *shared,
+                     int M, int H, int E, int I, int top_k, uint16_t *out,
+                     const flint_moe_debug *dbg, void *ws, size_t ws_bytes,
+                     void *stream);
+
+/* The MoE block on NVFP4 experts for any M >= 1 with grouped MFMA GEMMs
+ * (page "vllm.models.flint.ops.moe", flint_moe, grouped branch). */
+int flint_moe_grouped(const uint16_t *x, const uint16_t *router,
+                      const flint_nvfp4_experts *w, const flint_shared_expert *shared,
+                      int M, int H, int E, int I, int top_k, uint16_t *out,
+                      const flint_moe_debug *dbg, void *ws, size_t ws_bytes,
+                      void *stream);
+
+/* The MoE block on BF16 experts for decode-size batches, 1 <= M <= 64
+ * (page "vllm.models.flint.ops.moe", flint_moe_bf16_decode). */
+int flint_moe_bf16_decode(const uint16_t *x, const uint16_t *router,
+                          const flint_bf16_experts *w, const flint_shared_expert *shared,
+                          int M, int H, int E, int I, int top_k, uint16_t *out,
+                          const flint_moe_debug *dbg, void *ws, size_t ws_bytes,
+                          void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLINT_MOE_H */

@@ -1,0 +1,245 @@
+// C ABI of libflint_moe: argument validation, workspace layout, dispatch.
+// Everything here runs on the host; kernels live in the .hip files.
+#include <hip/hip_runtime.h>
+
+#include "../../include/flint_moe.h"
+#include "internal.hpp"
+
+namespace flint {
+
+static thread_local int g_last_hip_error = 0;
+
+static int hip_status(hipError_t e) {
+  if (e == hipSuccess) return FLINT_OK;
+  g_last_hip_error = (int)e;
+  return FLINT_ERR_HIP;
+}
+
+static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+Workspace carve_workspace(void *base, int M, int H, int E, int I, int SI, int top_k) {
+  Workspace w{};
+  size_t off = 0;
+  char *b = static_cast<char *>(base);
+  auto take = [&](size_t bytes) -> void * {
+    void *p = b ? b + off : nullptr;
+    off = align_up(off + bytes, 256);
+    return p;
+  };
+  const size_t P = (size_t)M * top_k;
+  w.counters = static_cast<int32_t *>(take(sizeof(int32_t) * kCounterWords));
+  w.logits = static_cast<uint16_t *>(take(2 * (size_t)M * E));
+  w.ids = static_cast<int32_t *>(take(4 * P));
+  w.tw = static_cast<float *>(take(4 * P));
+  w.plan.n_active = static_cast<int32_t *>(take(16));
+  w.plan.active = static_cast<int32_t *>(take(4 * (size_t)E));
+  w.plan.offs = static_cast<int32_t *>(take(4 * ((size_t)E + 1)));
+  w.plan.pairs = static_cast<int32_t *>(take(4 * P));
+  w.act = static_cast<uint16_t *>(take(2 * P * I));
+  w.y = static_cast<uint16_t *>(take(2 * P * H));
+  w.sact = static_cast<uint16_t *>(take(2 * (size_t)M * (SI > 0 ? SI : 0)));
+  w.sh = static_cast<uint16_t *>(take(2 * (size_t)M * H));
+  w.bytes = off;
+  return w;
+}
+
+}  // namespace flint
+
+using namespace flint;
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool route_h_ok(int H) { return H == 256 || H == 512 || H == 1024 || H == 2048 || H == 4096; }
+
+int check_common(int M, int H, int E, int I, int top_k) {
+  if (M < 0 || H <= 0 || E <= 0 || I <= 0) return FLINT_ERR_SHAPE;
+  if (top_k < 1 || top_k > E || E > kMaxExperts) return FLINT_ERR_SHAPE;
+  if ((long)M * top_k > (long)kMaxDecodePairs) return FLINT_ERR_SHAPE;
+  if (M > kMaxDecodeM) return FLINT_ERR_SHAPE;
+  if (!decode_shape_supported(H, I)) return FLINT_ERR_SHAPE;
+  return FLINT_OK;
+}
+
+int check_shared(const flint_shared_expert *sh, int H) {
+  if (!sh || !sh->w_gu) return FLINT_OK;
+  if (!sh->w_down) return FLINT_ERR_NULL;
+  if (!aligned16(sh->w_gu) || !aligned16(sh->w_down)) return FLINT_ERR_ALIGN;
+  if (!decode_shape_supported(H, sh->SI)) return FLINT_ERR_SHAPE;
+  return FLINT_OK;
+}
+
+// The decode pipeline shared by the NVFP4 and BF16 experts.
+int run_decode(int fmt, const uint16_t *x, const uint16_t *router, const void *w13,
+               const uint8_t *s13, const float *a13, const void *w2, const uint8_t *s2,
+               const float *a2, const flint_shared_expert *shared, int M, int H, int E, int I,
+               int top_k, uint16_t *out, const flint_moe_debug *dbg, void *ws,
+               size_t ws_bytes, hipStream_t st) {
+  const bool has_shared = shared && shared->w_gu;
+  const int SI = has_shared ? shared->SI : 0;
+  Workspace W = carve_workspace(ws, M, H, E, I, SI, top_k);
+  if (W.bytes > ws_bytes) return FLINT_ERR_WORKSPACE;
+  if (M == 0) return FLINT_OK;
+
+  const bool forced = dbg && dbg->ids_in;
+  uint16_t *logits = (dbg && dbg->logits_out) ? dbg->logits_out : W.logits;
+  int32_t *ids = (dbg && dbg->ids_out) ? dbg->ids_out : W.ids;
+  float *tw = (dbg && dbg->tw_out) ? dbg->tw_out : W.tw;
+  uint16_t *act = (dbg && dbg->act_out) ? dbg->act_out : W.act;
+  uint16_t *y = (dbg && dbg->y_out) ? dbg->y_out : W.y;
+  uint16_t *sact = (dbg && dbg->sact_out) ? dbg->sact_out : W.sact;
+  uint16_t *sh = (dbg && dbg->sh_out) ? dbg->sh_out : W.sh;
+  const int max_slots = E < M * top_k ? E : M * top_k;
+  const size_t P = (size_t)M * top_k;
+
+  hipError_t e = hipSuccess;
+  const int32_t *ids_use = ids;
+  const float *tw_use = tw;
+  if (forced) {
+    ids_use = dbg->ids_in;
+    tw_use = dbg->tw_in;
+    if (dbg->ids_out) e = hipMemcpyAsync(dbg->ids_out, dbg->ids_in, 4 * P, hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess && dbg->tw_out)
+      e = hipMemcpyAsync(dbg->tw_out, dbg->tw_in, 4 * P, hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess) e = launch_plan(ids_use, M, E, top_k, W.plan, st);
+  } else {
+    e = launch_route(x, router, M, H, E, top_k, logits, ids, tw, W.counters, &W.plan, st);
+  }
+  if (e == hipSuccess)
+    e = launch_gate_up(fmt, x, w13, s13, a13, M, H, I, top_k, max_slots, &W.plan, act, st);
+  if (e == hipSuccess && has_shared)
+    e = launch_gate_up(kBf16, x, shared->w_gu, nullptr, nullptr, M, H, SI, 1, 1, nullptr, sact, st);
+  if (e == hipSuccess)
+    e = launch_down(fmt, act, w2, s2, a2, M, H, I, top_k, max_slots, &W.plan, y, st);
+  if (e == hipSuccess && has_shared)
+    e = launch_down(kBf16, sact, shared->w_down, nullptr, nullptr, M, H, SI, 1, 1, nullptr, sh, st);
+  if (e == hipSuccess)
+    e = launch_combine(y, tw_use, has_shared ? sh : nullptr, M, H, top_k, out, st);
+  return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *flint_status_str(int status) {
+  switch (status) {
+    case FLINT_OK: return "ok";
+    case FLINT_ERR_NULL: return "a required pointer is NULL";
+    case FLINT_ERR_SHAPE: return "unsupported or inconsistent sizes";
+    case FLINT_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    case FLINT_ERR_WORKSPACE: return "workspace missing or too small";
+    case FLINT_ERR_HIP: return "a HIP call failed";
+    default: return "unknown status";
+  }
+}
+
+int flint_last_hip_error(void) { return g_last_hip_error; }
+
+int flint_moe_workspace_bytes(int max_M, int H, int E, int I, int SI, int top_k, size_t *bytes) {
+  if (!bytes) return FLINT_ERR_NULL;
+  if (max_M < 0 || H <= 0 || E <= 0 || I <= 0 || SI < 0 || top_k < 1 || top_k > E ||
+      E > kMaxExperts)
+    return FLINT_ERR_SHAPE;
+  *bytes = carve_workspace(nullptr, max_M, H, E, I, SI, top_k).bytes;
+  return FLINT_OK;
+}
+
+int flint_moe_workspace_init(void *ws, size_t ws_bytes, void *stream) {
+  if (!ws) return FLINT_ERR_NULL;
+  if (!aligned16(ws)) return FLINT_ERR_ALIGN;
+  if (ws_bytes < sizeof(int32_t) * kCounterWords) return FLINT_ERR_WORKSPACE;
+  return hip_status(hipMemsetAsync(ws, 0, ws_bytes, (hipStream_t)stream));
+}
+
+int flint_nvfp4_dequant(const uint8_t *w, const uint8_t *s, int rows, int K, uint16_t *out,
+                        void *stream) {
+  if (rows < 0 || K <= 0 || K % 32) return FLINT_ERR_SHAPE;
+  if (rows == 0) return FLINT_OK;
+  if (!w || !s || !out) return FLINT_ERR_NULL;
+  if (!aligned16(w) || !aligned16(s) || !aligned16(out)) return FLINT_ERR_ALIGN;
+  return hip_status(launch_dequant(w, s, rows, K, out, (hipStream_t)stream));
+}
+
+int flint_moe_topk(const uint16_t *logits, int M, int E, int top_k, int32_t *ids, float *tw,
+                   float *scores, void *stream) {
+  if (M < 0 || E < 1 || E > kMaxExperts || top_k < 1 || top_k > E) return FLINT_ERR_SHAPE;
+  if (M == 0) return FLINT_OK;
+  if (!logits || !ids || !tw) return FLINT_ERR_NULL;
+  if (!aligned16(logits) || !aligned16(ids) || !aligned16(tw) || (scores && !aligned16(scores)))
+    return FLINT_ERR_ALIGN;
+  if (M == 0) return FLINT_OK;
+  return hip_status(launch_topk(logits, M, E, top_k, ids, tw, scores, (hipStream_t)stream));
+}
+
+int flint_moe_route(const uint16_t *x, const uint16_t *router, int M, int H, int E, int top_k,
+                    uint16_t *logits, int32_t *ids, float *tw, void *ws, size_t ws_bytes,
+                    void *stream) {
+  if (M < 0 || E < 1 || E > kMaxExperts || top_k < 1 || top_k > E || !route_h_ok(H) ||
+      M > (kCounterWords - 1) * kRouteTokens)
+    return FLINT_ERR_SHAPE;
+  if (M == 0) return FLINT_OK;
+  if (!x || !router || !ids || !tw) return FLINT_ERR_NULL;
+  if (!ws) return FLINT_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(router) || !aligned16(ids) || !aligned16(tw) ||
+      (logits && !aligned16(logits)) || !aligned16(ws))
+    return FLINT_ERR_ALIGN;
+  Workspace W = carve_workspace(ws, M, H, E, 1, 0, top_k);
+  if (W.bytes > ws_bytes) return FLINT_ERR_WORKSPACE;
+  if (M == 0) return FLINT_OK;
+  return hip_status(launch_route(x, router, M, H, E, top_k, logits ? logits : W.logits, ids, tw,
+                                 W.counters, nullptr, (hipStream_t)stream));
+}
+
+int flint_moe_decode(const uint16_t *x, const uint16_t *router, const flint_nvfp4_experts *w,
+                     const flint_shared_expert *shared, int M, int H, int E, int I, int top_k,
+                     uint16_t *out, const flint_moe_debug *dbg, void *ws, size_t ws_bytes,
+                     void *stream) {
+  const bool forced = dbg && dbg->ids_in;
+  int st = check_common(M, H, E, I, top_k);
+  if (st) return st;
+  if (M == 0) return FLINT_OK;  // nothing to compute; no pointer is used
+  if (!x || !w || !out || (!forced && !router)) return FLINT_ERR_NULL;
+  if (!w->w13 || !w->s13 || !w->a13 || !w->w2 || !w->s2 || !w->a2) return FLINT_ERR_NULL;
+  if (forced && !dbg->tw_in) return FLINT_ERR_NULL;
+  if (!ws) return FLINT_ERR_WORKSPACE;
+  if ((st = check_shared(shared, H))) return st;
+  if (!aligned16(x) || (router && !aligned16(router)) || !aligned16(out) || !aligned16(ws) ||
+      !aligned16(w->w13) || !aligned16(w->s13) || !aligned16(w->a13) || !aligned16(w->w2) ||
+      !aligned16(w->s2) || !aligned16(w->a2))
+    return FLINT_ERR_ALIGN;
+  return run_decode(kNvfp4, x, router, w->w13, w->s13, w->a13, w->w2, w->s2, w->a2, shared, M,
+                    H, E, I, top_k, out, dbg, ws, ws_bytes, (hipStream_t)stream);
+}
+
+int flint_moe_bf16_decode(const uint16_t *x, const uint16_t *router, const flint_bf16_experts *w,
+                          const flint_shared_expert *shared, int M, int H, int E, int I,
+                          int top_k, uint16_t *out, const flint_moe_debug *dbg, void *ws,
+                          size_t ws_bytes, void *stream) {
+  const bool forced = dbg && dbg->ids_in;
+  int st = check_common(M, H, E, I, top_k);
+  if (st) return st;
+  if (M == 0) return FLINT_OK;  // nothing to compute; no pointer is used
+  if (!x || !w || !out || (!forced && !router)) return FLINT_ERR_NULL;
+  if (!w->w13 || !w->w2) return FLINT_ERR_NULL;
+  if (forced && !dbg->tw_in) return FLINT_ERR_NULL;
+  if (!ws) return FLINT_ERR_WORKSPACE;
+  if ((st = check_shared(shared, H))) return st;
+  if (!aligned16(x) || (router && !aligned16(router)) || !aligned16(out) || !aligned16(ws) ||
+      !aligned16(w->w13) || !aligned16(w->w2))
+    return FLINT_ERR_ALIGN;
+  return run_decode(kBf16, x, router, w->w13, nullptr, nullptr, w->w2, nullptr, nullptr, shared,
+                    M, H, E, I, top_k, out, dbg, ws, ws_bytes, (hipStream_t)stream);
+}
+
+int flint_moe_grouped(const uint16_t *x, const uint16_t *router, const flint_nvfp4_experts *w,
+                      const flint_shared_expert *shared, int M, int H, int E, int I, int top_k,
+                      uint16_t *out, const flint_moe_debug *dbg, void *ws, size_t ws_bytes,
+                      void *stream) {
+  (void)x; (void)router; (void)w; (void)shared; (void)M; (void)H; (void)E; (void)I;
+  (void)top_k; (void)out; (void)dbg; (void)ws; (void)ws_bytes; (void)stream;
+  return FLINT_ERR_SHAPE;
+}
+
+}  // extern "C"

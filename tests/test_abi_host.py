@@ -1,0 +1,115 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/flint_moe.h declares, and rejects bad arguments with
+the documented status codes before queueing any GPU work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import nvfp4_w4a16_routed_amd as fm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flint_moe.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(flint_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared() == sorted(fm.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = fm.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    L = fm.lib()
+    for st in (0, -1, -2, -3, -4, -5):
+        assert L.flint_status_str(st).decode()
+    assert L.flint_status_str(123).decode() == "unknown status"
+
+
+def test_workspace_bytes():
+    n = fm.flint_moe_workspace_bytes(64, 2048, 128, 768, 768, 8)
+    assert n > 0 and n % 256 == 0
+    assert fm.flint_moe_workspace_bytes(64, 2048, 128, 768, 768, 8) >= \
+        fm.flint_moe_workspace_bytes(8, 2048, 128, 768, 768, 8)
+    with pytest.raises(fm.FlintError):
+        fm.flint_moe_workspace_bytes(8, 2048, 300, 768, 768, 8)  # E > 256
+    with pytest.raises(fm.FlintError):
+        fm.flint_moe_workspace_bytes(8, 2048, 8, 768, 768, 9)    # top_k > E
+
+
+# Fake, never-dereferenced device addresses: every case below must be
+# rejected by host validation before anything is queued.
+A = ctypes.c_void_p(0x10000)
+MIS = ctypes.c_void_p(0x10008)
+
+
+def _experts(ptr=A):
+    return fm.NvFp4Experts(ptr, ptr, ptr, ptr, ptr, ptr)
+
+
+def _decode(x=A, router=A, w=None, shared=None, M=8, H=2048, E=128, I=768, k=8, out=A,
+            dbg=None, ws=A, ws_bytes=1 << 30):
+    w = _experts() if w is None else w
+    return fm.lib().flint_moe_decode(x, router, ctypes.byref(w),
+                                     ctypes.byref(shared) if shared else None, M, H, E, I, k,
+                                     out, ctypes.byref(dbg) if dbg else None, ws, ws_bytes, None)
+
+
+def test_decode_rejects_bad_arguments():
+    assert _decode(x=None) == -1
+    assert _decode(out=None) == -1
+    assert _decode(w=fm.NvFp4Experts(A, None, A, A, A, A)) == -1
+    assert _decode(ws=None) == -4
+    assert _decode(ws_bytes=1024) == -4
+    assert _decode(M=65) == -2             # decode is for M <= 64
+    assert _decode(k=0) == -2
+    assert _decode(E=257) == -2
+    assert _decode(k=200, E=256) == -2     # M * top_k beyond the decode plan
+    assert _decode(H=1000) == -2
+    assert _decode(I=700) == -2
+    assert _decode(x=MIS) == -3
+    assert _decode(w=_experts(MIS)) == -3
+    sh = fm.SharedExpert(A, None, 768)
+    assert _decode(shared=sh) == -1
+    sh = fm.SharedExpert(A, A, 700)
+    assert _decode(shared=sh) == -2
+    dbg = fm.MoeDebug(A, None, None, None, None, None, None, None, None)
+    assert _decode(dbg=dbg) == -1          # forced ids without weights
+    assert _decode(M=0, x=None) == 0       # empty batch: valid no-op
+
+
+def test_bf16_decode_and_grouped_reject_bad_arguments():
+    L = fm.lib()
+    w = fm.Bf16Experts(A, None)
+    assert L.flint_moe_bf16_decode(A, A, ctypes.byref(w), None, 8, 2048, 128, 768, 8, A, None, A,
+                                   1 << 30, None) == -1
+    w = fm.Bf16Experts(MIS, A)
+    assert L.flint_moe_bf16_decode(A, A, ctypes.byref(w), None, 8, 2048, 128, 768, 8, A, None, A,
+                                   1 << 30, None) == -3
+
+
+def test_topk_route_dequant_reject_bad_arguments():
+    L = fm.lib()
+    assert L.flint_moe_topk(A, 4, 300, 8, A, A, None, None) == -2
+    assert L.flint_moe_topk(A, 4, 16, 17, A, A, None, None) == -2
+    assert L.flint_moe_topk(None, 4, 16, 8, A, A, None, None) == -1
+    assert L.flint_moe_topk(MIS, 4, 16, 8, A, A, None, None) == -3
+    assert L.flint_moe_topk(None, 0, 16, 8, None, None, None, None) == 0
+    assert L.flint_moe_route(A, A, 4, 1000, 16, 8, None, A, A, A, 1 << 30, None) == -2
+    assert L.flint_moe_route(A, A, 4, 2048, 16, 8, None, A, A, None, 1 << 30, None) == -4
+    assert L.flint_moe_route(A, A, 4, 2048, 16, 8, None, A, A, A, 64, None) == -4
+    assert L.flint_nvfp4_dequant(A, A, 4, 33, A, None) == -2
+    assert L.flint_nvfp4_dequant(None, A, 4, 32, A, None) == -1
+    assert L.flint_nvfp4_dequant(A, MIS, 4, 32, A, None) == -3
+    assert L.flint_moe_workspace_init(None, 1 << 20, None) == -1
+    assert L.flint_moe_workspace_init(A, 16, None) == -4

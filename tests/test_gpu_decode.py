@@ -1,0 +1,237 @@
+"""GPU parity of the HIP path against the CPU oracle (needs an MI355X).
+
+Every call goes through the C ABI (ctypes binding); inputs come from the
+seeded generator; expected values come from the oracle only.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import gpu_helpers as G
+
+pytestmark = pytest.mark.gpu
+
+fm = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _binding():
+    global fm
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import nvfp4_w4a16_routed_amd as m
+    m.lib()
+    fm = m
+    oracle.set_threads(16)
+    yield
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------- dequant
+
+def test_dequant_exhaustive_bit_exact():
+    _say("dequant exhaustive 16 codes x 256 scales")
+    K = 32
+    codes = np.arange(K) % 16
+    packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+    w = np.ascontiguousarray(np.tile(packed, (256, 1)))
+    s = np.ascontiguousarray(np.repeat(np.arange(256, dtype=np.uint8)[:, None], K // 16, axis=1))
+    got = G.host(fm.flint_nvfp4_dequant(G.dev(w), G.dev(s)))
+    torch.cuda.synchronize()
+    want = oracle.nvfp4_dequant(w, s)
+    gv, wv = G.bf(got), G.bf(want)
+    nan = np.isnan(wv)
+    assert np.array_equal(np.isnan(gv), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+
+
+def test_dequant_random_matrix_bit_exact():
+    _say("dequant random 96 x 2048")
+    inp = synth.nvfp4_experts(5, 1, 2048, 48)
+    w = np.ascontiguousarray(inp["w13"][0])
+    s = np.ascontiguousarray(inp["s13"][0])
+    got = G.host(fm.flint_nvfp4_dequant(G.dev(w), G.dev(s)))
+    assert np.array_equal(got, oracle.nvfp4_dequant(w, s))
+
+
+# --------------------------------------------------------------- top-k
+
+def _topk_gpu(lg, k):
+    ids, tw, sc = fm.flint_moe_topk(G.dev(lg), k, want_scores=True)
+    torch.cuda.synchronize()
+    return G.host(ids), G.host(tw), G.host(sc)
+
+
+def _same_f32(a, b):
+    a, b = np.asarray(a, np.float32), np.asarray(b, np.float32)
+    return np.array_equal(np.isnan(a), np.isnan(b)) and np.array_equal(
+        a[~np.isnan(a)].view(np.uint32), b[~np.isnan(b)].view(np.uint32))
+
+
+def test_router_scores_exhaustive_over_bf16():
+    """All 65536 bf16 logits: fp32 sigmoid scores bit-exact with the oracle."""
+    _say("topk exhaustive scores: 256 rows x 256 experts, top_k=256")
+    lg = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(256, 256)
+    ids, tw, sc = _topk_gpu(lg, 256)
+    rids, rtw, rsc = oracle.topk(lg, 256)
+    assert np.array_equal(ids, rids)
+    assert _same_f32(sc, rsc)
+    assert _same_f32(tw, rtw)
+
+
+@pytest.mark.parametrize("E,k", [(8, 1), (8, 8), (32, 4), (128, 8), (256, 8), (256, 64), (3, 2)])
+def test_topk_bit_exact_with_ties(E, k):
+    _say(f"topk E={E} k={k}")
+    rng = np.random.default_rng(E * 100 + k)
+    M = 301
+    vals = rng.choice(np.float32([-3, -1.5, -0.0, 0.0, 0.25, 0.5, 2, 7]), size=(M, E))
+    vals = vals + rng.integers(0, 2, (M, E)) * rng.standard_normal((M, E)).astype(np.float32)
+    lg = torch.from_numpy(vals.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    ids, tw, sc = _topk_gpu(lg, k)
+    rids, rtw, rsc = oracle.topk(lg, k)
+    assert np.array_equal(ids, rids)
+    assert _same_f32(tw, rtw) and _same_f32(sc, rsc)
+
+
+def test_topk_special_values():
+    row = np.array([[0x8000, 0x0000, 0xFF80, 0x7F80, 0x7FC0, 0xFFC0, 0x3F80, 0x3F80]],
+                   dtype=np.uint16)
+    ids, tw, sc = _topk_gpu(row, 8)
+    rids, rtw, rsc = oracle.topk(row, 8)
+    assert np.array_equal(ids, rids)
+    assert _same_f32(sc, rsc) and np.isnan(tw).all()
+
+
+# --------------------------------------------------------------- route
+
+@pytest.mark.parametrize("M,E,H", [(1, 32, 2048), (37, 128, 2048), (8, 256, 256), (700, 128, 512)])
+def test_route_logits_and_topk(M, E, H):
+    _say(f"route M={M} E={E} H={H}")
+    inp = synth.make_small(100 + M, M=M, H=H, E=E, I=128, SI=0, top_k=8)
+    ws = fm.make_workspace(M, H, E, 128, 0, 8)
+    x, router = G.dev(inp["x"]), G.dev(inp["router"])
+    logits = torch.empty((M, E), dtype=torch.int16, device="cuda")
+    ids, tw = fm.flint_moe_route(x, router, 8, ws, logits=logits)
+    torch.cuda.synchronize()
+    lg = G.host(logits)
+    ref = oracle.logits(inp["x"], inp["router"])
+    diff = np.abs(G.bf(lg) - G.bf(ref))
+    assert np.all(diff <= G.ulp_bf16(G.bf(ref))), "logit beyond one bf16 ulp"
+    rids, rtw, _ = oracle.topk(lg, 8)
+    assert np.array_equal(G.host(ids), rids)
+    assert _same_f32(G.host(tw), rtw)
+    # a second call reuses the workspace counters (reset by the kernels)
+    ids2, tw2 = fm.flint_moe_route(x, router, 8, ws, logits=logits)
+    torch.cuda.synchronize()
+    assert np.array_equal(G.host(ids2), rids)
+
+
+# -------------------------------------------------------- decode blocks
+
+def _stagewise(inp, r, path):
+    """Checks every stage of a GPU run against the oracle fed with the GPU's
+    own upstream values; returns the oracle's end-to-end result."""
+    cfg = inp["cfg"]
+    k, I, H = cfg["top_k"], cfg["I"], cfg["H"]
+    label = cfg["name"]
+    # routing: ids / tw bit-exact given the GPU's logits
+    ref_lg = oracle.logits(inp["x"], inp["router"])
+    assert np.all(np.abs(G.bf(r["logits"]) - G.bf(ref_lg)) <= G.ulp_bf16(G.bf(ref_lg)))
+    rids, rtw, _ = oracle.topk(r["logits"], k)
+    assert np.array_equal(r["ids"], rids) and _same_f32(r["tw"], rtw)
+    # gate/up on the GPU's routing
+    act, det = oracle.gate_up(inp["x"], r["ids"], k, inp, I, want_detail=True)
+    G.check_act(r["act"], act, det, label)
+    # down on the GPU's act
+    y, ydet = oracle.down(r["act"], r["ids"], inp, H, want_detail=True)
+    G.check_y(r["y"], y, ydet, label)
+    sh = None
+    if "sgu" in inp:
+        sact, sh_ref, sdet = oracle.shared_expert(inp["x"], inp["sgu"], inp["sdown"], True)
+        G.check_act(r["sact"], sact, sdet["gate_up"], label + " shared")
+        zeros = np.zeros(cfg["M"], np.int32)
+        sh2, shdet = oracle.down(r["sact"], zeros, dict(bw2=inp["sdown"][None]), H, True)
+        G.check_y(r["sh"], sh2, shdet, label + " shared")
+        sh = r["sh"]
+    # combine: bit-exact on the GPU's y, tw and shared output
+    out_c, _ = oracle.combine(r["y"], r["tw"], sh, k)
+    assert np.array_equal(r["out"], out_c), "combine differs"
+    # end to end against the oracle's own routing
+    full = oracle.moe_block(inp)
+    same = np.all(full["ids"] == r["ids"], axis=1)
+    ulps = G.end_to_end_ulps(r["out"], full, k, rows=same)
+    _say(f"{label}: tokens {cfg['M']}, near-tie flips {int((~same).sum())}, "
+         f"max ulp(m) {ulps.max() if ulps.size else 0:.3f}, "
+         f"mean nonzero {np.mean(ulps > 0) if ulps.size else 0:.4f}")
+    assert ulps.size == 0 or ulps.max() <= 2.0
+    return full
+
+
+@pytest.mark.parametrize("M,E,k,H,I,SI", [
+    (1, 8, 2, 256, 128, 128),
+    (5, 16, 4, 256, 128, 128),
+    (13, 32, 8, 256, 256, 0),
+    (64, 16, 8, 512, 128, 128),
+    (3, 4, 4, 2048, 768, 768),
+])
+def test_decode_small_stagewise(M, E, k, H, I, SI):
+    _say(f"decode small M={M} E={E} k={k} H={H} I={I} SI={SI}")
+    inp = synth.make_small(200 + M + E, M=M, H=H, E=E, I=I, SI=SI, top_k=k, router_std=0.3)
+    r = G.run_block(fm, inp, "decode")
+    _stagewise(inp, r, "decode")
+
+
+@pytest.mark.parametrize("M,E,k,H,I,SI", [(4, 8, 2, 256, 128, 128), (9, 16, 4, 512, 256, 256)])
+def test_bf16_decode_small_stagewise(M, E, k, H, I, SI):
+    _say(f"bf16 decode small M={M} E={E} k={k} H={H} I={I}")
+    inp = synth.make_small(300 + M, M=M, H=H, E=E, I=I, SI=SI, top_k=k, experts="bf16",
+                           router_std=0.3)
+    r = G.run_block(fm, inp, "bf16_decode")
+    _stagewise(inp, r, "bf16_decode")
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+def test_decode_full_size_configs(cfg):
+    c = synth.CONFIGS[cfg]
+    _say(f"full-size config {cfg}: {c['name']}")
+    inp = synth.make_inputs(cfg)
+    path = "bf16_decode" if c["experts"] == "bf16" else "decode"
+    r = G.run_block(fm, inp, path)
+    _stagewise(inp, r, path)
+
+
+def test_forced_routing_and_determinism():
+    _say("decode forced routing + determinism")
+    inp = synth.make_small(401, M=6, H=256, E=16, I=128, SI=128, top_k=4, router_std=0.3)
+    r1 = G.run_block(fm, inp, "decode")
+    r2 = G.run_block(fm, inp, "decode")
+    for key in r1:
+        assert np.array_equal(r1[key], r2[key]), key
+    # forced routing with the oracle's own ids / tw reproduces the same stages
+    ref = oracle.moe_block(inp)
+    rf = G.run_block(fm, inp, "decode", forced=(ref["ids"], ref["tw"]))
+    act, det = oracle.gate_up(inp["x"], ref["ids"], 4, inp, 128, want_detail=True)
+    G.check_act(rf["act"], act, det, "forced")
+    out_c, _ = oracle.combine(rf["y"], ref["tw"], rf["sh"], 4)
+    assert np.array_equal(rf["out"], out_c)
+
+
+def test_decode_edge_cases():
+    _say("decode edge cases: M=0, top_k=E, E=1")
+    # M = 0: valid no-op
+    inp = synth.make_small(501, M=1, H=256, E=8, I=128, SI=128, top_k=2)
+    d = G.device_inputs(inp)
+    ws = fm.make_workspace(1, 256, 8, 128, 128, 2)
+    x0 = torch.empty((0, 256), dtype=torch.int16, device="cuda")
+    out0 = fm.flint_moe_decode(x0, d["router"], G.experts_of(d), G.shared_of(d), 2, ws)
+    assert out0.shape == (0, 256)
+    # every expert selected, and a single expert
+    for (E, k) in ((8, 8), (1, 1)):
+        inp = synth.make_small(510 + E, M=7, H=256, E=E, I=128, SI=128, top_k=k, router_std=0.3)
+        r = G.run_block(fm, inp, "decode")
+        _stagewise(inp, r, "decode")
