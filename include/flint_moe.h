@@ -98,7 +98,17 @@ typedef struct {
   uint16_t *y_out;       /* [M*top_k, H] bf16 */
   uint16_t *sact_out;    /* [M, SI] bf16 shared-expert activations */
   uint16_t *sh_out;      /* [M, H] bf16 shared-expert output */
+  /* Stage timing: NULL, or an array of FLINT_STAGE_EVENTS hipEvent_t
+   * (caller-created).  events[i] is recorded on `stream` just before stage i
+   * is queued and events[FLINT_STAGE_EVENTS - 1] after the last stage, so
+   * hipEventElapsedTime(events[i], events[i + 1]) times stage i.  Stages:
+   * 0 routing, 1 routed gate/up, 2 shared gate/up, 3 routed down,
+   * 4 shared down, 5 combine (absent stages take no time).  The decode
+   * entry points record them; others ignore the field. */
+  void **stage_events;
 } flint_moe_debug;
+
+#define FLINT_STAGE_EVENTS 7
 
 /* Status code -> static string. */
 const char *flint_status_str(int status);

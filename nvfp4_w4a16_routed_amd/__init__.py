@@ -57,10 +57,14 @@ class SharedExpert(ctypes.Structure):
     _fields_ = [("w_gu", P), ("w_down", P), ("SI", I32)]
 
 
+FLINT_STAGE_EVENTS = 7
+STAGES = ("route", "gate_up", "shared_gate_up", "down", "shared_down", "combine")
+
+
 class MoeDebug(ctypes.Structure):
     _fields_ = [("ids_in", P), ("tw_in", P), ("logits_out", P), ("ids_out", P),
                 ("tw_out", P), ("act_out", P), ("y_out", P), ("sact_out", P),
-                ("sh_out", P)]
+                ("sh_out", P), ("stage_events", ctypes.POINTER(P))]
 
 
 _lib = None
@@ -186,9 +190,13 @@ def _shared_struct(shared):
 
 
 def _debug_struct(debug):
+    """debug: dict of tensors named after MoeDebug's fields; "stage_events" may
+    hold a ctypes array of FLINT_STAGE_EVENTS hipEvent_t handles."""
     if not debug:
         return None
-    return MoeDebug(*(_ptr(debug.get(f)) for f, _ in MoeDebug._fields_))
+    vals = [_ptr(debug.get(f)) for f, _ in MoeDebug._fields_[:-1]]
+    ev = debug.get("stage_events")
+    return MoeDebug(*vals, ctypes.cast(ev, ctypes.POINTER(P)) if ev is not None else None)
 
 
 def _moe_call(name, wstruct, x, router, shared, I, E, top_k, ws, out, debug, stream):

@@ -27,7 +27,8 @@ Workspace carve_workspace(void *base, int M, int H, int E, int I, int SI, int to
     return p;
   };
   const size_t P = (size_t)M * top_k;
-  w.counters = static_cast<int32_t *>(take(sizeof(int32_t) * kCounterWords));
+  w.sync = static_cast<DecodeSync *>(take(sizeof(DecodeSync)));
+  w.route_counters = static_cast<int32_t *>(take(sizeof(int32_t) * kRouteCounterWords));
   w.logits = static_cast<uint16_t *>(take(2 * (size_t)M * E));
   w.ids = static_cast<int32_t *>(take(4 * P));
   w.tw = static_cast<float *>(take(4 * P));
@@ -62,11 +63,12 @@ int check_common(int M, int H, int E, int I, int top_k) {
   return FLINT_OK;
 }
 
-int check_shared(const flint_shared_expert *sh, int H) {
+int check_shared(const flint_shared_expert *sh, int H, int I) {
   if (!sh || !sh->w_gu) return FLINT_OK;
   if (!sh->w_down) return FLINT_ERR_NULL;
   if (!aligned16(sh->w_gu) || !aligned16(sh->w_down)) return FLINT_ERR_ALIGN;
   if (!decode_shape_supported(H, sh->SI)) return FLINT_ERR_SHAPE;
+  if (sh->SI != I) return FLINT_ERR_SHAPE;  // the decode kernel's shared expert is I wide
   return FLINT_OK;
 }
 
@@ -90,32 +92,41 @@ int run_decode(int fmt, const uint16_t *x, const uint16_t *router, const void *w
   uint16_t *y = (dbg && dbg->y_out) ? dbg->y_out : W.y;
   uint16_t *sact = (dbg && dbg->sact_out) ? dbg->sact_out : W.sact;
   uint16_t *sh = (dbg && dbg->sh_out) ? dbg->sh_out : W.sh;
-  const int max_slots = E < M * top_k ? E : M * top_k;
-  const size_t P = (size_t)M * top_k;
-
-  hipError_t e = hipSuccess;
-  const int32_t *ids_use = ids;
-  const float *tw_use = tw;
-  if (forced) {
-    ids_use = dbg->ids_in;
-    tw_use = dbg->tw_in;
-    if (dbg->ids_out) e = hipMemcpyAsync(dbg->ids_out, dbg->ids_in, 4 * P, hipMemcpyDeviceToDevice, st);
-    if (e == hipSuccess && dbg->tw_out)
-      e = hipMemcpyAsync(dbg->tw_out, dbg->tw_in, 4 * P, hipMemcpyDeviceToDevice, st);
-    if (e == hipSuccess) e = launch_plan(ids_use, M, E, top_k, W.plan, st);
-  } else {
-    e = launch_route(x, router, M, H, E, top_k, logits, ids, tw, W.counters, &W.plan, st);
-  }
-  if (e == hipSuccess)
-    e = launch_gate_up(fmt, x, w13, s13, a13, M, H, I, top_k, max_slots, &W.plan, act, st);
-  if (e == hipSuccess && has_shared)
-    e = launch_gate_up(kBf16, x, shared->w_gu, nullptr, nullptr, M, H, SI, 1, 1, nullptr, sact, st);
-  if (e == hipSuccess)
-    e = launch_down(fmt, act, w2, s2, a2, M, H, I, top_k, max_slots, &W.plan, y, st);
-  if (e == hipSuccess && has_shared)
-    e = launch_down(kBf16, sact, shared->w_down, nullptr, nullptr, M, H, SI, 1, 1, nullptr, sh, st);
-  if (e == hipSuccess)
-    e = launch_combine(y, tw_use, has_shared ? sh : nullptr, M, H, top_k, out, st);
+  void **ev = dbg ? dbg->stage_events : nullptr;
+  auto mark = [&](int i) {
+    if (ev && ev[i]) hipEventRecord((hipEvent_t)ev[i], st);
+  };
+  DecodeArgs a{};
+  a.x = x;
+  a.router = router;
+  a.w13 = static_cast<const uint8_t *>(w13);
+  a.s13 = s13;
+  a.a13 = a13;
+  a.w2 = static_cast<const uint8_t *>(w2);
+  a.s2 = s2;
+  a.a2 = a2;
+  a.sgu = has_shared ? reinterpret_cast<const uint8_t *>(shared->w_gu) : nullptr;
+  a.sdown = has_shared ? reinterpret_cast<const uint8_t *>(shared->w_down) : nullptr;
+  a.ids_in = forced ? dbg->ids_in : nullptr;
+  a.tw_in = forced ? dbg->tw_in : nullptr;
+  a.logits = logits;
+  a.ids = forced && !(dbg->ids_out) ? const_cast<int32_t *>(dbg->ids_in) : ids;
+  a.tw = forced && !(dbg->tw_out) ? const_cast<float *>(dbg->tw_in) : tw;
+  a.act = act;
+  a.y = y;
+  a.sact = sact;
+  a.sh = sh;
+  a.out = out;
+  a.sync = W.sync;
+  a.M = M;
+  a.H = H;
+  a.E = E;
+  a.I = I;
+  a.top_k = top_k;
+  // One kernel runs every stage: the stage events bracket the whole of it.
+  mark(0);
+  hipError_t e = launch_decode_fused(fmt, a, st);
+  for (int i = 1; i < FLINT_STAGE_EVENTS; ++i) mark(i);
   return hip_status(e);
 }
 
@@ -149,7 +160,7 @@ int flint_moe_workspace_bytes(int max_M, int H, int E, int I, int SI, int top_k,
 int flint_moe_workspace_init(void *ws, size_t ws_bytes, void *stream) {
   if (!ws) return FLINT_ERR_NULL;
   if (!aligned16(ws)) return FLINT_ERR_ALIGN;
-  if (ws_bytes < sizeof(int32_t) * kCounterWords) return FLINT_ERR_WORKSPACE;
+  if (ws_bytes < kCounterBytes) return FLINT_ERR_WORKSPACE;
   return hip_status(hipMemsetAsync(ws, 0, ws_bytes, (hipStream_t)stream));
 }
 
@@ -177,7 +188,7 @@ int flint_moe_route(const uint16_t *x, const uint16_t *router, int M, int H, int
                     uint16_t *logits, int32_t *ids, float *tw, void *ws, size_t ws_bytes,
                     void *stream) {
   if (M < 0 || E < 1 || E > kMaxExperts || top_k < 1 || top_k > E || !route_h_ok(H) ||
-      M > (kCounterWords - 1) * kRouteTokens)
+      M > kCtrRouteAll * kRouteTokens)
     return FLINT_ERR_SHAPE;
   if (M == 0) return FLINT_OK;
   if (!x || !router || !ids || !tw) return FLINT_ERR_NULL;
@@ -189,7 +200,7 @@ int flint_moe_route(const uint16_t *x, const uint16_t *router, int M, int H, int
   if (W.bytes > ws_bytes) return FLINT_ERR_WORKSPACE;
   if (M == 0) return FLINT_OK;
   return hip_status(launch_route(x, router, M, H, E, top_k, logits ? logits : W.logits, ids, tw,
-                                 W.counters, nullptr, (hipStream_t)stream));
+                                 W.route_counters, nullptr, (hipStream_t)stream));
 }
 
 int flint_moe_decode(const uint16_t *x, const uint16_t *router, const flint_nvfp4_experts *w,
@@ -204,7 +215,7 @@ int flint_moe_decode(const uint16_t *x, const uint16_t *router, const flint_nvfp
   if (!w->w13 || !w->s13 || !w->a13 || !w->w2 || !w->s2 || !w->a2) return FLINT_ERR_NULL;
   if (forced && !dbg->tw_in) return FLINT_ERR_NULL;
   if (!ws) return FLINT_ERR_WORKSPACE;
-  if ((st = check_shared(shared, H))) return st;
+  if ((st = check_shared(shared, H, I))) return st;
   if (!aligned16(x) || (router && !aligned16(router)) || !aligned16(out) || !aligned16(ws) ||
       !aligned16(w->w13) || !aligned16(w->s13) || !aligned16(w->a13) || !aligned16(w->w2) ||
       !aligned16(w->s2) || !aligned16(w->a2))
@@ -225,7 +236,7 @@ int flint_moe_bf16_decode(const uint16_t *x, const uint16_t *router, const flint
   if (!w->w13 || !w->w2) return FLINT_ERR_NULL;
   if (forced && !dbg->tw_in) return FLINT_ERR_NULL;
   if (!ws) return FLINT_ERR_WORKSPACE;
-  if ((st = check_shared(shared, H))) return st;
+  if ((st = check_shared(shared, H, I))) return st;
   if (!aligned16(x) || (router && !aligned16(router)) || !aligned16(out) || !aligned16(ws) ||
       !aligned16(w->w13) || !aligned16(w->w2))
     return FLINT_ERR_ALIGN;

@@ -71,20 +71,129 @@ __device__ __forceinline__ float swiglu(float g, float u) {
 }
 
 // ------------------------------------------------------- wave reductions
+//
+// Reductions within aligned groups of L lanes (L a power of two <= 64) with
+// DPP: quad permutes, half-row and row mirrors inside a 16-lane row (after
+// which every lane of the row holds the row's result), then row_bcast15 /
+// row_bcast31 across rows (after which the LAST lane of each 32- or 64-lane
+// group holds the group's result).  Each step combines two partial results
+// in a fixed order, so the result does not depend on timing.
 
-// Sum over aligned groups of L lanes (L a power of two <= 64); every lane of
-// a group ends with the group's sum.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f32(float v, float old = 0.0f) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                               __builtin_bit_cast(int, v), CTRL,
+                                                               ROW_MASK, 0xF, ROW_MASK == 0xF));
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_i32(int v, int old = 0) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, ROW_MASK == 0xF);
+}
+
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8 lanes
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16 lanes
+constexpr int kDppBcast15 = 0x142;    // lane 15 of each row -> next row
+constexpr int kDppBcast31 = 0x143;    // lane 31 -> rows 2 and 3
+
+// Sum over groups of L lanes; valid in every lane for L <= 16, in the last
+// lane of the group for L = 32 and 64.
 template <int L>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int o = L / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  static_assert(L >= 1 && L <= 64 && (L & (L - 1)) == 0, "group size");
+  if constexpr (L >= 2) v += dpp_f32<kDppXor1>(v);
+  if constexpr (L >= 4) v += dpp_f32<kDppXor2>(v);
+  if constexpr (L >= 8) v += dpp_f32<kDppHalfMirror>(v);
+  if constexpr (L >= 16) v += dpp_f32<kDppMirror>(v);
+  if constexpr (L >= 32) v += dpp_f32<kDppBcast15, 0xA>(v);  // rows 1, 3 += rows 0, 2
+  if constexpr (L >= 64) v += dpp_f32<kDppBcast31, 0xC>(v);  // rows 2, 3 += lane 31
   return v;
 }
 
+// Maximum over the wave, returned uniformly (from lane 63).
 __device__ __forceinline__ int wave_max_i32(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = max(v, dpp_i32<kDppXor1>(v));
+  v = max(v, dpp_i32<kDppXor2>(v));
+  v = max(v, dpp_i32<kDppHalfMirror>(v));
+  v = max(v, dpp_i32<kDppMirror>(v));
+  v = max(v, dpp_i32<kDppBcast15, 0xA>(v, v));
+  v = max(v, dpp_i32<kDppBcast31, 0xC>(v, v));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// ------------------------------------------------- cross-wave signalling
+//
+// Data exchanged between waves of one grid (which may run on different
+// XCDs, each with its own L2) is written and read with device-scope
+// ("agent") relaxed atomic accesses: such stores are performed at the
+// device's coherence point and such loads read from it, so no L2 writeback
+// or invalidate is needed.  A producer publishes by waiting until its
+// stores are performed (s_waitcnt vmcnt(0)) and then incrementing an arrival
+// counter; a consumer polls the counter and then reads the data.
+
+template <typename T>
+__device__ __forceinline__ void st_dev(T *p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_dev(const T *p) {
+  return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16 bytes (8-byte aligned) read at device scope.
+__device__ __forceinline__ u32x4_t ld_dev16(const void *p) {
+  const uint64_t *q = reinterpret_cast<const uint64_t *>(p);
+  const uint64_t a = ld_dev(q), b = ld_dev(q + 1);
+  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
+}
+
+__device__ __forceinline__ int atomic_add_agent(int *p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int load_agent(const int *p) { return ld_dev(p); }
+__device__ __forceinline__ void store_agent(int *p, int v) { st_dev(p, v); }
+
+// Waits until every store this wave issued has been performed.
+__device__ __forceinline__ void stores_performed() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // keeps the compiler's order
+  __builtin_amdgcn_s_waitcnt(0x0F70);                     // vmcnt(0) (expcnt, lgkmcnt: any)
+}
+
+// Publishes this wave's device-scope stores: one arrival on *cnt; returns
+// the count before it (uniform over the wave).
+__device__ __forceinline__ int arrive(int *cnt) {
+  stores_performed();
+  int prev = 0;
+  if ((threadIdx.x & (kWave - 1)) == 0) prev = atomic_add_agent(cnt, 1);
+  prev = __builtin_amdgcn_readfirstlane(prev);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");  // later reads stay after the count
+  return prev;
+}
+
+// Publishes this wave's device-scope stores with one arrival on *cnt,
+// without waiting for the count.
+__device__ __forceinline__ void arrive_nowait(int *cnt) {
+  stores_performed();
+  if ((threadIdx.x & (kWave - 1)) == 0)
+    __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Spins until *p >= target, polling at a fixed short interval (for a
+// flag only one wave polls).
+__device__ __forceinline__ void wait_flag(const int *p, int target) {
+  while (load_agent(p) < target) __builtin_amdgcn_s_sleep(1);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");  // keeps the compiler's order
+}
+
+// Spins until *p >= target (the producers are running waves of the same
+// grid that never wait on this wave, so the wait ends), backing off.
+__device__ __forceinline__ void wait_at_least(const int *p, int target) {
+  int naps = 1;
+  while (load_agent(p) < target) {
+    for (int i = 0; i < naps; ++i) __builtin_amdgcn_s_sleep(2);
+    naps = naps < 16 ? naps * 2 : 16;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");  // keeps the compiler's order
 }
 
 // ------------------------------------------------------------ memory ops

@@ -13,13 +13,50 @@ enum WeightFmt { kNvfp4 = 0, kBf16 = 1 };
 constexpr int kRouteTokens = 8;
 constexpr int kRouteExperts = 4;
 // Decode plan limits: pairs (M * top_k) per call and experts.
-constexpr int kMaxDecodePairs = 1024;
+constexpr int kMaxDecodePairs = 512;
 constexpr int kMaxExperts = 256;
 constexpr int kMaxDecodeM = 64;
-// Counter words at the start of the workspace.
-constexpr int kCounterWords = 4096;
-// Counter index of the route kernel's all-groups counter.
-constexpr int kCtrRouteAll = kCounterWords - 1;
+// Largest grid of the fused decode kernel (blocks).
+constexpr int kMaxDecodeBlocks = 2048;
+// Fan-in of the first level of the decode kernel's phase barrier.
+constexpr int kBarrierGroups = 32;
+// Synchronisation words of the fused decode kernel, each counter on its own
+// 128-byte line.  They are zero between calls: every counter is reset by
+// its last arrival or its single consumer.
+constexpr int kLine = 32;  // ints per 128-byte line
+struct DecodeSync {
+  int route_cnt[kMaxDecodeM][kLine];  // routing items done, per token
+  int topk_done[kLine];               // tokens whose top-k is done
+  uint32_t active[kLine];             // touched-expert bitmask (words 0..7)
+  int rb_cnt[512][kLine];             // down items done, per combine row block
+  int grp_cnt[kBarrierGroups][kLine]; // blocks done with the gate/up phase, per group
+  int top_cnt[kLine];                 // groups done with the gate/up phase
+  int go[kMaxDecodeBlocks][kLine];    // per-block phase flag (1: routed, 2: gate/up done)
+};
+
+// The route kernel's arrival counters follow the decode block: token groups
+// use indices 0 .. kCtrRouteAll - 1, kCtrRouteAll counts finished groups.
+constexpr int kRouteCounterWords = 2048;
+constexpr int kCtrRouteAll = kRouteCounterWords - 1;
+constexpr size_t kCounterBytes = sizeof(DecodeSync) + sizeof(int) * kRouteCounterWords;
+
+// Arguments of the fused decode kernel (device pointers).
+struct DecodeArgs {
+  const uint16_t *x, *router;
+  const uint8_t *w13, *s13;
+  const float *a13;
+  const uint8_t *w2, *s2;
+  const float *a2;
+  const uint8_t *sgu, *sdown;   // shared expert (bf16), NULL = none
+  const int32_t *ids_in;        // forced routing, NULL = route
+  const float *tw_in;
+  uint16_t *logits;
+  int32_t *ids;
+  float *tw;
+  uint16_t *act, *y, *sact, *sh, *out;
+  DecodeSync *sync;
+  int M, H, E, I, top_k;
+};
 
 // Routing plan of one call (device pointers into the workspace):
 //   n_active    number of experts used by at least one pair
@@ -35,7 +72,8 @@ struct Plan {
 
 // Device buffers a call needs, carved out of the caller's workspace.
 struct Workspace {
-  int32_t *counters;   // [kCounterWords], zero between calls
+  DecodeSync *sync;         // zero between calls
+  int32_t *route_counters;  // [kRouteCounterWords], zero between calls
   uint16_t *logits;    // [M, E]
   int32_t *ids;        // [M, k]
   float *tw;           // [M, k]
@@ -67,20 +105,11 @@ hipError_t launch_route(const uint16_t *x, const uint16_t *router, int M, int H,
 hipError_t launch_plan(const int32_t *ids, int M, int E, int top_k, const Plan &plan,
                        hipStream_t st);
 
-// Gate/up + SwiGLU of every routed pair (decode), or of the shared expert
-// (plan == NULL: one job covering tokens 0..M-1, weights w13 of one expert).
-hipError_t launch_gate_up(int fmt, const uint16_t *x, const void *w13, const uint8_t *s13,
-                          const float *a13, int M, int H, int I, int top_k, int max_slots,
-                          const Plan *plan, uint16_t *act, hipStream_t st);
+// The whole decode block in one cooperative launch (fmt of the routed
+// experts; the shared expert, if any, is bf16 with SI == I).
+hipError_t launch_decode_fused(int fmt, const DecodeArgs &a, hipStream_t st);
 
-hipError_t launch_down(int fmt, const uint16_t *act, const void *w2, const uint8_t *s2,
-                       const float *a2, int M, int H, int I, int top_k, int max_slots,
-                       const Plan *plan, uint16_t *y, hipStream_t st);
-
-hipError_t launch_combine(const uint16_t *y, const float *tw, const uint16_t *sh, int M,
-                          int H, int top_k, uint16_t *out, hipStream_t st);
-
-// Whether the decode kernels are compiled for this (H, I).
+// Whether the decode kernel is compiled for this (H, I) (both formats).
 bool decode_shape_supported(int H, int I);
 
 }  // namespace flint

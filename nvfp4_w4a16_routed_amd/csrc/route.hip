@@ -192,7 +192,7 @@ route_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ router
         }
       }
       acc = group_sum<kWave>(acc);
-      if (lane == 0) logits[(size_t)(t0 + ti) * E + e] = (uint16_t)f32_to_bf16(acc);
+      if (lane == kWave - 1) logits[(size_t)(t0 + ti) * E + e] = (uint16_t)f32_to_bf16(acc);
     }
   }
   // Publish this block's logits, then count arrivals of the token group.

@@ -1,0 +1,215 @@
+// Per-lane row dot products of the expert GEMVs (gfx950, wave64).
+//
+// A weight row of K elements is split in 16-byte chunks (32 NVFP4 codes or 8
+// bf16 values).  LPR lanes share a row; lane q of a row owns chunks
+// q + LPR * i (i < CPL), so every load instruction reads LPR * 16 contiguous
+// bytes of the row and 64 / LPR rows are in flight per instruction.
+#pragma once
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace flint {
+
+constexpr int pow2_divisor(int n, int cap) {
+  int p = 1;
+  while (p * 2 <= cap && n % (p * 2) == 0) p *= 2;
+  return p;
+}
+constexpr int pow2_ceil(int n) {
+  int p = 1;
+  while (p < n) p *= 2;
+  return p;
+}
+
+// Lane mapping of a row.  NVFP4 rows: one chunk per lane on a power-of-two
+// group of lanes (a 24-chunk row, I = 768, uses 24 of 32 lanes; the idle
+// lanes contribute zero), which keeps the per-lane vector slice at 64 bytes.
+// BF16 rows: LPR the largest power-of-two divisor of the chunk count, every
+// lane busy.
+template <int FMT, int K>
+struct RowMap {
+  static constexpr int CE = FMT == kNvfp4 ? 32 : 8;        // elements per chunk
+  static constexpr int NC = K / CE;                          // chunks per row
+  static constexpr int LPR = FMT == kNvfp4 ? (NC >= kWave ? kWave : pow2_ceil(NC))
+                                           : pow2_divisor(NC, kWave);  // lanes per row
+  static constexpr int CPL = (NC + LPR - 1) / LPR;           // chunks per lane
+  static constexpr bool PAD = LPR * CPL != NC;               // some lanes idle
+  static constexpr int RS = kWave / LPR;                     // rows per slice
+  static constexpr int ROW_BYTES = FMT == kNvfp4 ? K / 2 : K * 2;
+  static_assert(K % CE == 0, "row length");
+  static_assert(!PAD || CPL == 1, "padded rows hold one chunk per lane");
+  __device__ static bool active(int q, int i) { return !PAD || q + LPR * i < NC; }
+};
+
+// Weight registers of one row for one lane: raw 16-byte chunks and, for
+// NVFP4, the two E4M3 block-scale bytes of each chunk.
+template <int FMT, int K>
+struct RowRegs {
+  using Map = RowMap<FMT, K>;
+  u32x4_t raw[Map::CPL];
+  uint32_t sc[Map::CPL];
+};
+
+// The lane's part of a bf16 vector matching one chunk of a row.
+template <int FMT>
+struct VecChunk {
+  static constexpr int U4 = FMT == kNvfp4 ? 4 : 1;  // 16-byte loads per chunk
+  u32x4_t v[U4];
+};
+
+// Makes the compiler treat the weight registers as changed here, so it
+// does not hoist their conversion to bf16 out of a loop over pairs (that
+// would hold every row's converted codes at once and exceed the register
+// budget); converting per pair costs half an instruction per element.
+template <int FMT, int K>
+__device__ __forceinline__ void opaque(RowRegs<FMT, K> &r) {
+#pragma unroll
+  for (int i = 0; i < RowMap<FMT, K>::CPL; ++i) {
+    asm volatile("" : "+v"(r.raw[i]));
+    if constexpr (FMT == kNvfp4) asm volatile("" : "+v"(r.sc[i]));
+  }
+}
+
+template <int FMT, int K>
+__device__ __forceinline__ void load_row(RowRegs<FMT, K> &r, const uint8_t *wrow,
+                                         const uint8_t *srow, int q) {
+  using Map = RowMap<FMT, K>;
+#pragma unroll
+  for (int i = 0; i < Map::CPL; ++i) {
+    const int c = q + Map::LPR * i;
+    r.raw[i] = u32x4_t{0, 0, 0, 0};
+    r.sc[i] = 0;
+    if (Map::active(q, i)) {
+      r.raw[i] = load16_stream(wrow + (size_t)c * 16);
+      if constexpr (FMT == kNvfp4) r.sc[i] = load_u16(srow + (size_t)c * 2);
+    }
+  }
+}
+
+// Where a vector is read from: an input in global memory (plain loads),
+// data other waves of the grid wrote (device-scope loads; see the
+// signalling notes in common.hpp), or a copy in LDS.
+enum VecSrc { kSrcGlobal = 0, kSrcDevice = 1, kSrcLds = 2 };
+
+// Chunk i of the lane's part of vector `vec` (K elements).
+template <int FMT, int K, int SRC>
+__device__ __forceinline__ void load_chunk(VecChunk<FMT> &x, const uint16_t *vec, int q, int i) {
+  using Map = RowMap<FMT, K>;
+  const uint16_t *p = vec + (size_t)(q + Map::LPR * i) * Map::CE;
+  const bool on = Map::active(q, i);
+#pragma unroll
+  for (int u = 0; u < VecChunk<FMT>::U4; ++u) {
+    if (!on)
+      x.v[u] = u32x4_t{0, 0, 0, 0};
+    else if constexpr (SRC == kSrcDevice)
+      x.v[u] = ld_dev16(p + 8 * u);
+    else
+      x.v[u] = load16(p + 8 * u);  // global or LDS (address space inferred)
+  }
+}
+
+// Partial dot product of one chunk of a row with the matching vector part.
+// NVFP4: codes -> bf16 pairs (hardware converter), bf16 dot2 into fp32 per
+// 16-element block, times the block's E4M3 scale (exact), summed in fp32.
+template <int FMT>
+__device__ __forceinline__ float chunk_dot(const u32x4_t &raw, uint32_t sc, const VecChunk<FMT> &x) {
+  if constexpr (FMT == kNvfp4) {
+    float part[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x4_t va = x.v[2 * h];
+      const u32x4_t vb = x.v[2 * h + 1];
+      uint32_t w0[4], w1[4];
+      fp4x8_to_bf16(raw[2 * h], w0);
+      fp4x8_to_bf16(raw[2 * h + 1], w1);
+      float p = dot2_bf16(w0[0], va[0], 0.0f);
+      p = dot2_bf16(w0[1], va[1], p);
+      p = dot2_bf16(w0[2], va[2], p);
+      p = dot2_bf16(w0[3], va[3], p);
+      p = dot2_bf16(w1[0], vb[0], p);
+      p = dot2_bf16(w1[1], vb[1], p);
+      p = dot2_bf16(w1[2], vb[2], p);
+      p = dot2_bf16(w1[3], vb[3], p);
+      part[h] = p;
+    }
+    return part[0] * e4m3_to_f32(sc & 0xffu) + part[1] * e4m3_to_f32((sc >> 8) & 0xffu);
+  } else {
+    (void)sc;
+    const u32x4_t va = x.v[0];
+    float p = dot2_bf16(raw[0], va[0], 0.0f);
+    p = dot2_bf16(raw[1], va[1], p);
+    p = dot2_bf16(raw[2], va[2], p);
+    return dot2_bf16(raw[3], va[3], p);
+  }
+}
+
+// All chunks of the lane's part of one vector.
+template <int FMT, int K>
+struct VecRegs {
+  VecChunk<FMT> c[RowMap<FMT, K>::CPL];
+};
+
+template <int FMT, int K, int SRC>
+__device__ __forceinline__ void load_vec(VecRegs<FMT, K> &x, const uint16_t *vec, int q) {
+#pragma unroll
+  for (int i = 0; i < RowMap<FMT, K>::CPL; ++i) load_chunk<FMT, K, SRC>(x.c[i], vec, q, i);
+}
+
+// Per-lane partial dot products of NR rows with a vector held in registers.
+template <int FMT, int K, int NR>
+__device__ __forceinline__ void rows_dot_regs(const RowRegs<FMT, K> (&rows)[NR],
+                                              const VecRegs<FMT, K> &x, float (&acc)[NR]) {
+#pragma unroll
+  for (int r = 0; r < NR; ++r) acc[r] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < RowMap<FMT, K>::CPL; ++i)
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      acc[r] += chunk_dot<FMT>(rows[r].raw[i], rows[r].sc[i], x.c[i]);
+      // One row's converted codes live at a time (keeps the register budget).
+      if constexpr (FMT == kNvfp4) __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Per-lane partial dot products of NR rows (all with the same lane mapping)
+// with one vector, chunk by chunk so each vector chunk is loaded once.
+template <int FMT, int K, int SRC, int NR>
+__device__ __forceinline__ void rows_dot(const RowRegs<FMT, K> (&rows)[NR], const uint16_t *vec,
+                                         int q, float (&acc)[NR]) {
+  using Map = RowMap<FMT, K>;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) acc[r] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < Map::CPL; ++i) {
+    VecChunk<FMT> x;
+    load_chunk<FMT, K, SRC>(x, vec, q, i);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      acc[r] += chunk_dot<FMT>(rows[r].raw[i], rows[r].sc[i], x);
+      if constexpr (FMT == kNvfp4) __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// Gate/up geometry: row pairs per wave item, whole row slices (2 NVFP4 row
+// pairs = 4.6 KB at H = 2048, 1 bf16 row pair = 8 KB).
+template <int FMT, int H>
+struct GateUpGeo {
+  using Map = RowMap<FMT, H>;
+  static constexpr int RP_MIN = FMT == kNvfp4 ? 2 : 1;
+  static constexpr int RP = Map::RS >= RP_MIN ? Map::RS : RP_MIN;
+  static constexpr int NSL = RP / Map::RS;
+};
+
+// Down geometry: output rows per wave item, whole slices (8 NVFP4 rows =
+// 3.4 KB at I = 768, 4 bf16 rows = 6 KB).
+template <int FMT, int I>
+struct DownGeo {
+  using Map = RowMap<FMT, I>;
+  static constexpr int RW_MIN = FMT == kNvfp4 ? 8 : 4;
+  static constexpr int RW = Map::RS >= RW_MIN ? Map::RS : RW_MIN;
+  static constexpr int NSL = RW / Map::RS;
+};
+
+}  // namespace flint
