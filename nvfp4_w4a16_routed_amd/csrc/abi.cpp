@@ -2,6 +2,8 @@
 // Everything here runs on the host; kernels live in the .hip files.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "../../include/flint_moe.h"
 #include "internal.hpp"
 
@@ -16,6 +18,16 @@ static int hip_status(hipError_t e) {
 }
 
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Sequence numbers of decode calls: unique per call (1 .. 2^31 - 1, then
+// around again), so completion flags left by earlier calls never match.
+static std::atomic<uint32_t> g_seq{0};
+static int next_seq() {
+  for (;;) {
+    const uint32_t v = (g_seq.fetch_add(1, std::memory_order_relaxed) + 1u) & 0x7fffffffu;
+    if (v != 0) return (int)v;
+  }
+}
 
 Workspace carve_workspace(void *base, int M, int H, int E, int I, int SI, int top_k) {
   Workspace w{};
@@ -118,6 +130,7 @@ int run_decode(int fmt, const uint16_t *x, const uint16_t *router, const void *w
   a.sh = sh;
   a.out = out;
   a.sync = W.sync;
+  a.seq = next_seq();
   a.M = M;
   a.H = H;
   a.E = E;
@@ -125,7 +138,7 @@ int run_decode(int fmt, const uint16_t *x, const uint16_t *router, const void *w
   a.top_k = top_k;
   // One kernel runs every stage: the stage events bracket the whole of it.
   mark(0);
-  hipError_t e = launch_decode_fused(fmt, a, st);
+  hipError_t e = launch_decode(fmt, a, st);
   for (int i = 1; i < FLINT_STAGE_EVENTS; ++i) mark(i);
   return hip_status(e);
 }

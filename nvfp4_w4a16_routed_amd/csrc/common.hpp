@@ -159,41 +159,23 @@ __device__ __forceinline__ void stores_performed() {
   __builtin_amdgcn_s_waitcnt(0x0F70);                     // vmcnt(0) (expcnt, lgkmcnt: any)
 }
 
-// Publishes this wave's device-scope stores: one arrival on *cnt; returns
-// the count before it (uniform over the wave).
-__device__ __forceinline__ int arrive(int *cnt) {
-  stores_performed();
-  int prev = 0;
-  if ((threadIdx.x & (kWave - 1)) == 0) prev = atomic_add_agent(cnt, 1);
-  prev = __builtin_amdgcn_readfirstlane(prev);
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");  // later reads stay after the count
-  return prev;
-}
-
-// Publishes this wave's device-scope stores with one arrival on *cnt,
-// without waiting for the count.
-__device__ __forceinline__ void arrive_nowait(int *cnt) {
-  stores_performed();
-  if ((threadIdx.x & (kWave - 1)) == 0)
-    __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Spins until *p >= target, polling at a fixed short interval (for a
-// flag only one wave polls).
-__device__ __forceinline__ void wait_flag(const int *p, int target) {
-  while (load_agent(p) < target) __builtin_amdgcn_s_sleep(1);
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");  // keeps the compiler's order
-}
-
-// Spins until *p >= target (the producers are running waves of the same
-// grid that never wait on this wave, so the wait ends), backing off.
-__device__ __forceinline__ void wait_at_least(const int *p, int target) {
+// Spins until *p >= target, backing off briefly between polls.  The
+// producers are running blocks that never wait on the caller, so the wait
+// ends; as a guard against a workspace whose counters were not zero, it
+// gives up after about 2^22 polls (seconds) so the kernel still ends.
+__device__ __forceinline__ bool wait_at_least(const int *p, int target) {
   int naps = 1;
-  while (load_agent(p) < target) {
+  bool ok = false;
+  for (int it = 0; it < (1 << 22); ++it) {
+    if (load_agent(p) >= target) {
+      ok = true;
+      break;
+    }
     for (int i = 0; i < naps; ++i) __builtin_amdgcn_s_sleep(2);
-    naps = naps < 16 ? naps * 2 : 16;
+    naps = naps < 4 ? naps * 2 : 4;
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");  // keeps the compiler's order
+  return ok;
 }
 
 // ------------------------------------------------------------ memory ops

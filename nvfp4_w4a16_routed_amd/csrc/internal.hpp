@@ -16,22 +16,21 @@ constexpr int kRouteExperts = 4;
 constexpr int kMaxDecodePairs = 512;
 constexpr int kMaxExperts = 256;
 constexpr int kMaxDecodeM = 64;
-// Largest grid of the fused decode kernel (blocks).
-constexpr int kMaxDecodeBlocks = 2048;
-// Fan-in of the first level of the decode kernel's phase barrier.
-constexpr int kBarrierGroups = 32;
-// Synchronisation words of the fused decode kernel, each counter on its own
-// 128-byte line.  They are zero between calls: every counter is reset by
-// its last arrival or its single consumer.
-constexpr int kLine = 32;  // ints per 128-byte line
+// Decode kernel grid limits: blocks, waves, routing blocks, and the blocks
+// of its shared gate/up and shared down segments.
+constexpr int kMaxDecodeBlocks = 1024;
+constexpr int kMaxDecodeWaves = kMaxDecodeBlocks * 8;
+constexpr int kMaxRouteBlocks = 256;
+constexpr int kMaxSharedBlocks = 1024;
+// Completion flags of the decode kernel.  A flag holds the sequence number
+// of the call that set it (every call gets a new one), so flags never need
+// resetting.
 struct DecodeSync {
-  int route_cnt[kMaxDecodeM][kLine];  // routing items done, per token
-  int topk_done[kLine];               // tokens whose top-k is done
-  uint32_t active[kLine];             // touched-expert bitmask (words 0..7)
-  int rb_cnt[512][kLine];             // down items done, per combine row block
-  int grp_cnt[kBarrierGroups][kLine]; // blocks done with the gate/up phase, per group
-  int top_cnt[kLine];                 // groups done with the gate/up phase
-  int go[kMaxDecodeBlocks][kLine];    // per-block phase flag (1: routed, 2: gate/up done)
+  int go[kMaxDecodeBlocks][kMaxRouteBlocks];  // [block][routing block]: logits written
+  int sg[kMaxSharedBlocks];                   // shared gate/up block done
+  int sd[kMaxSharedBlocks];                   // shared down block done
+  int gw[kMaxDecodeWaves];                    // routed gate/up wave done
+  int dw[kMaxDecodeWaves];                    // routed down wave done
 };
 
 // The route kernel's arrival counters follow the decode block: token groups
@@ -40,7 +39,7 @@ constexpr int kRouteCounterWords = 2048;
 constexpr int kCtrRouteAll = kRouteCounterWords - 1;
 constexpr size_t kCounterBytes = sizeof(DecodeSync) + sizeof(int) * kRouteCounterWords;
 
-// Arguments of the fused decode kernel (device pointers).
+// Arguments of the decode kernel (device pointers).
 struct DecodeArgs {
   const uint16_t *x, *router;
   const uint8_t *w13, *s13;
@@ -55,6 +54,7 @@ struct DecodeArgs {
   float *tw;
   uint16_t *act, *y, *sact, *sh, *out;
   DecodeSync *sync;
+  int seq;  // call sequence number (never 0; unique per call)
   int M, H, E, I, top_k;
 };
 
@@ -105,9 +105,9 @@ hipError_t launch_route(const uint16_t *x, const uint16_t *router, int M, int H,
 hipError_t launch_plan(const int32_t *ids, int M, int E, int top_k, const Plan &plan,
                        hipStream_t st);
 
-// The whole decode block in one cooperative launch (fmt of the routed
-// experts; the shared expert, if any, is bf16 with SI == I).
-hipError_t launch_decode_fused(int fmt, const DecodeArgs &a, hipStream_t st);
+// The whole decode block in one launch (fmt of the routed experts; the
+// shared expert, if any, is bf16 with SI == I).
+hipError_t launch_decode(int fmt, const DecodeArgs &a, hipStream_t st);
 
 // Whether the decode kernel is compiled for this (H, I) (both formats).
 bool decode_shape_supported(int H, int I);

@@ -58,19 +58,6 @@ struct VecChunk {
   u32x4_t v[U4];
 };
 
-// Makes the compiler treat the weight registers as changed here, so it
-// does not hoist their conversion to bf16 out of a loop over pairs (that
-// would hold every row's converted codes at once and exceed the register
-// budget); converting per pair costs half an instruction per element.
-template <int FMT, int K>
-__device__ __forceinline__ void opaque(RowRegs<FMT, K> &r) {
-#pragma unroll
-  for (int i = 0; i < RowMap<FMT, K>::CPL; ++i) {
-    asm volatile("" : "+v"(r.raw[i]));
-    if constexpr (FMT == kNvfp4) asm volatile("" : "+v"(r.sc[i]));
-  }
-}
-
 template <int FMT, int K>
 __device__ __forceinline__ void load_row(RowRegs<FMT, K> &r, const uint8_t *wrow,
                                          const uint8_t *srow, int q) {
@@ -156,6 +143,16 @@ __device__ __forceinline__ void load_vec(VecRegs<FMT, K> &x, const uint16_t *vec
   for (int i = 0; i < RowMap<FMT, K>::CPL; ++i) load_chunk<FMT, K, SRC>(x.c[i], vec, q, i);
 }
 
+// A copy of one chunk of weight registers that the compiler must treat as
+// changed here: the caller converts codes to bf16 per use instead of
+// hoisting the conversion of every row out of a loop over vectors (that
+// would hold all rows' converted codes at once and exceed the register
+// budget; converting per use costs half an instruction per element).
+__device__ __forceinline__ u32x4_t opaque_chunk(u32x4_t raw) {
+  asm volatile("" : "+v"(raw));
+  return raw;
+}
+
 // Per-lane partial dot products of NR rows with a vector held in registers.
 template <int FMT, int K, int NR>
 __device__ __forceinline__ void rows_dot_regs(const RowRegs<FMT, K> (&rows)[NR],
@@ -166,7 +163,7 @@ __device__ __forceinline__ void rows_dot_regs(const RowRegs<FMT, K> (&rows)[NR],
   for (int i = 0; i < RowMap<FMT, K>::CPL; ++i)
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-      acc[r] += chunk_dot<FMT>(rows[r].raw[i], rows[r].sc[i], x.c[i]);
+      acc[r] += chunk_dot<FMT>(opaque_chunk(rows[r].raw[i]), rows[r].sc[i], x.c[i]);
       // One row's converted codes live at a time (keeps the register budget).
       if constexpr (FMT == kNvfp4) __builtin_amdgcn_sched_barrier(0);
     }
@@ -186,7 +183,7 @@ __device__ __forceinline__ void rows_dot(const RowRegs<FMT, K> (&rows)[NR], cons
     load_chunk<FMT, K, SRC>(x, vec, q, i);
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-      acc[r] += chunk_dot<FMT>(rows[r].raw[i], rows[r].sc[i], x);
+      acc[r] += chunk_dot<FMT>(opaque_chunk(rows[r].raw[i]), rows[r].sc[i], x);
       if constexpr (FMT == kNvfp4) __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -211,5 +208,50 @@ struct DownGeo {
   static constexpr int RW = Map::RS >= RW_MIN ? Map::RS : RW_MIN;
   static constexpr int NSL = RW / Map::RS;
 };
+
+// Weights of a gate/up wave item: rows[s] = gate row of slice s, rows[NSL + s]
+// its up row (RP row pairs n_base .. n_base + RP - 1).
+template <int FMT, int H, int I>
+struct GateUpW {
+  RowRegs<FMT, H> rows[2 * GateUpGeo<FMT, H>::NSL];
+};
+
+template <int FMT, int H, int I>
+__device__ __forceinline__ void gate_up_load(GateUpW<FMT, H, I> &W, const uint8_t *wexp,
+                                             const uint8_t *sexp, int n_base) {
+  using Map = RowMap<FMT, H>;
+  using Geo = GateUpGeo<FMT, H>;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = lane / Map::LPR, q = lane % Map::LPR;
+#pragma unroll
+  for (int s = 0; s < Geo::NSL; ++s) {
+    const int n = n_base + s * Map::RS + r;
+    load_row(W.rows[s], wexp + (size_t)n * Map::ROW_BYTES,
+             FMT == kNvfp4 ? sexp + (size_t)n * (H / 16) : nullptr, q);
+    load_row(W.rows[Geo::NSL + s], wexp + (size_t)(I + n) * Map::ROW_BYTES,
+             FMT == kNvfp4 ? sexp + (size_t)(I + n) * (H / 16) : nullptr, q);
+  }
+}
+
+// Weights of a down wave item: RW output rows h_base .. h_base + RW - 1.
+template <int FMT, int I>
+struct DownW {
+  RowRegs<FMT, I> rows[DownGeo<FMT, I>::NSL];
+};
+
+template <int FMT, int I>
+__device__ __forceinline__ void down_load(DownW<FMT, I> &W, const uint8_t *wexp,
+                                          const uint8_t *sexp, int h_base) {
+  using Map = RowMap<FMT, I>;
+  using Geo = DownGeo<FMT, I>;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = lane / Map::LPR, q = lane % Map::LPR;
+#pragma unroll
+  for (int s = 0; s < Geo::NSL; ++s) {
+    const int h = h_base + s * Map::RS + r;
+    load_row(W.rows[s], wexp + (size_t)h * Map::ROW_BYTES,
+             FMT == kNvfp4 ? sexp + (size_t)h * (I / 16) : nullptr, q);
+  }
+}
 
 }  // namespace flint
