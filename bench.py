@@ -3,15 +3,16 @@
 A step is one call of the whole block (router, top-k, routing plan, routed
 gate/up + SwiGLU, routed down, shared expert, combine) on one batch of
 seeded synthetic tokens, with every input already resident in HBM.  The
-default workload is decode of M=8 tokens against E=128 NVFP4 experts (H=2048,
-I=768, top_k=8, shared SwiGLU expert of width 768).  Weights are rotated over
-L layer copies so the working set exceeds twice the 256 MB Infinity Cache and
-weight bytes really come from HBM.
+headline workload is decode of M=8 tokens against E=128 NVFP4 experts
+(H=2048, I=768, top_k=8, shared SwiGLU expert of width 768).  Weights are
+rotated over L layer copies so the working set exceeds twice the 256 MB
+Infinity Cache and weight bytes really come from HBM.
 
 Prints one JSON line: tokens/s, the achieved HBM bandwidth over the step's
-algorithmic bytes, the roofline of the dominant kernel (timed with HIP
-events over the timed region), and the CPU oracle's throughput on a bounded
-sample of the same workload.
+algorithmic bytes, the roofline of the dominant kernel (its duration timed
+with HIP events on the stream it runs on), the CPU oracle's throughput on a
+bounded sample of the same workload and, unless --no-grouped, the prefill
+workload (M=4096) on the grouped MFMA path with its own roofline.
 """
 from __future__ import annotations
 
@@ -27,7 +28,9 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+METRIC = "MoE-layer tokens/sec at M=8 decode; achieved HBM GB/s vs peak"
 
 
 def _args():
@@ -35,10 +38,12 @@ def _args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=1, help="workload index (0-3 decode)")
+    ap.add_argument("--config", type=int, default=1, help="decode workload index (0-3)")
     ap.add_argument("--layers", type=int, default=0, help="weight copies rotated (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-grouped", action="store_true", help="skip the M=4096 grouped line")
+    ap.add_argument("--grouped-steps", type=int, default=30)
     return ap.parse_args()
 
 
@@ -89,6 +94,16 @@ def algorithmic_bytes(cfg: dict, U: int) -> dict:
                 x=x, out=out, total=router + U * (gate_up + down) + shared + x + out)
 
 
+def flops(cfg: dict) -> dict:
+    """Multiply-add work of one step (2 flops each)."""
+    M, H, E, I, SI, k = cfg["M"], cfg["H"], cfg["E"], cfg["I"], cfg["SI"], cfg["top_k"]
+    P = M * k
+    f = dict(router=2 * M * E * H, gate_up=2 * P * 2 * I * H, down=2 * P * H * I,
+             shared_gate_up=2 * M * 2 * SI * H, shared_down=2 * M * H * SI)
+    f["total"] = sum(f.values())
+    return f
+
+
 def cpu_baseline(inp: dict, seconds: float) -> dict:
     import oracle
     cfg = inp["cfg"]
@@ -106,21 +121,9 @@ def cpu_baseline(inp: dict, seconds: float) -> dict:
                       f"routing, all stages) on the host CPU, {el:.1f} s"}
 
 
-def main():
-    a = _args()
-    if a.gpus != 1:
-        print(f"bench.py measures one GPU only (--gpus {a.gpus} requested): the Flint MoE "
-              "block here runs on a single MI355X; multi-GPU sharding is a design note, not a "
-              "measured path.", file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-
-    import nvfp4_w4a16_routed_amd as fm
-    import synth
-
-    fm.lib()
-    cfg_idx = a.config
+def run(fm, synth, torch, cfg_idx: int, path: str, steps: int, warmup: int, layers: int):
+    """Times `steps` calls of `path` on workload cfg_idx.  Returns a dict with
+    the step time, per-stage event times and the workload's sizes."""
     inp = synth.make_inputs(cfg_idx)
     cfg = inp["cfg"]
     M, H, E, I, SI, k = cfg["M"], cfg["H"], cfg["E"], cfg["I"], cfg["SI"], cfg["top_k"]
@@ -135,110 +138,164 @@ def main():
     keys = ["w13", "s13", "a13", "w2", "s2", "a2"] if nvfp4 else ["bw13", "bw2"]
     base = {kk: up(inp[kk]) for kk in keys + ["router", "sgu", "sdown"]}
     per_layer = sum(v.numel() * v.element_size() for v in base.values())
-    L = a.layers or max(2, int(np.ceil(2 * 256e6 / per_layer)) + 1)
-    layers = [base] + [{kk: v.clone() for kk, v in base.items()} for _ in range(L - 1)]
+    L = layers or max(2, int(np.ceil(2 * 256e6 / per_layer)) + 1)
+    lays = [base] + [{kk: v.clone() for kk, v in base.items()} for _ in range(L - 1)]
     x = up(inp["x"])
+    del inp
     out = torch.empty((M, H), dtype=torch.int16, device=dev)
     ws = fm.make_workspace(M, H, E, I, SI, k)
     ids = torch.empty((M, k), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
-    L_ = fm.lib()
-    fn = L_.flint_moe_decode if nvfp4 else L_.flint_moe_bf16_decode
-
-    # Prebuilt C arguments per layer (marshalling once, outside the timing).
+    lib = fm.lib()
+    fn = {"decode": lib.flint_moe_decode, "grouped": lib.flint_moe_grouped,
+          "bf16_decode": lib.flint_moe_bf16_decode}[path]
     keep = []
 
     def c_args(lay, dbg=None):
         if nvfp4:
-            ws_ = fm.nvfp4_experts_struct(*(lay[kk] for kk in keys))
+            w = fm.nvfp4_experts_struct(*(lay[kk] for kk in keys))
         else:
-            ws_ = fm.Bf16Experts(fm._ptr(lay["bw13"]), fm._ptr(lay["bw2"]))
+            w = fm.Bf16Experts(fm._ptr(lay["bw13"]), fm._ptr(lay["bw2"]))
         sh = fm.SharedExpert(fm._ptr(lay["sgu"]), fm._ptr(lay["sdown"]), SI)
-        keep.extend([ws_, sh, dbg])
-        return (fm._ptr(x), fm._ptr(lay["router"]), ctypes.byref(ws_), ctypes.byref(sh), M, H,
-                E, I, k, fm._ptr(out), ctypes.byref(dbg) if dbg is not None else None,
-                fm._ptr(ws), ws.numel(), sp)
+        keep.extend([w, sh, dbg])
+        return (fm._ptr(x), fm._ptr(lay["router"]), ctypes.byref(w), ctypes.byref(sh), M, H, E,
+                I, k, fm._ptr(out), ctypes.byref(dbg) if dbg is not None else None, fm._ptr(ws),
+                ws.numel(), sp)
 
-    plain = [c_args(lay) for lay in layers]
-
-    # Routing of the workload (touched experts) from one call.
+    plain = [c_args(lay) for lay in lays]
+    # touched experts of the workload, from one call
     dbg = fm.MoeDebug(None, None, None, fm._ptr(ids), None, None, None, None, None, None)
-    assert fn(*c_args(layers[0], dbg)) == 0
+    assert fn(*c_args(lays[0], dbg)) == 0
     torch.cuda.synchronize()
     U = int(np.unique(ids.cpu().numpy()).size)
-    nbytes = algorithmic_bytes(cfg, U)
 
-    # Pass A: the timed region for the step throughput.
-    for i in range(a.warmup):
+    # Pass A: back-to-back steps (the step throughput)
+    for i in range(warmup):
         assert fn(*plain[i % L]) == 0
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for i in range(a.steps):
+    for i in range(steps):
         fn(*plain[i % L])
     e1.record(stream)
     torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / a.steps
+    ms_step = e0.elapsed_time(e1) / steps
 
-    # Pass B: the same steps with HIP events around every stage.
+    # Pass B: the same steps with HIP events around every stage (kernel)
     hev = HipEvents()
     nev = fm.FLINT_STAGE_EVENTS
-    evs = [hev.create(nev) for _ in range(a.steps)]
+    evs = [hev.create(nev) for _ in range(steps)]
     staged = []
-    for i in range(a.steps):
+    for i in range(steps):
         d = fm.MoeDebug(None, None, None, None, None, None, None, None, None,
                         ctypes.cast(evs[i], ctypes.POINTER(ctypes.c_void_p)))
-        staged.append(c_args(layers[i % L], d))
+        staged.append(c_args(lays[i % L], d))
     torch.cuda.synchronize()
-    for i in range(a.steps):
+    for i in range(steps):
         fn(*staged[i])
     torch.cuda.synchronize()
     stage_ms = np.zeros(nev - 1)
-    for i in range(a.steps):
+    for i in range(steps):
         for s in range(nev - 1):
             stage_ms[s] += hev.elapsed_ms(evs[i][s], evs[i][s + 1])
-    stage_ms /= a.steps
+    stage_ms /= steps
     for e in evs:
         hev.destroy(e)
+    del lays, plain, staged, keep
+    torch.cuda.empty_cache()
+    return dict(cfg=cfg, U=U, L=L, per_layer=per_layer, ms_step=ms_step, stage_ms=stage_ms)
 
-    # Dominant kernel: the decode path is one fused kernel (routing, expert
-    # GEMVs, shared expert and combine), so its bytes are the step's
-    # algorithmic bytes and its duration the span of the stage events.
-    kern_ms = float(stage_ms.sum())
-    dom_name = "decode_kernel"
-    dom_bytes = nbytes["total"]
-    dom_gbps = dom_bytes / (kern_ms * 1e-3) / 1e9
-    value = M / (ms_step * 1e-3)
-    gbps = nbytes["total"] / (ms_step * 1e-3) / 1e9
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {a.gpus} requested): the Flint MoE "
+              "block here runs on a single MI355X; sharding across GPUs is a design note, not a "
+              "measured path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import nvfp4_w4a16_routed_amd as fm
+    import synth
+
+    fm.lib()
+    cfg_idx = a.config
+    path = "bf16_decode" if synth.CONFIGS[cfg_idx]["experts"] == "bf16" else "decode"
+    if cfg_idx == 4:
+        path = "grouped"
+    r = run(fm, synth, torch, cfg_idx, path, a.steps, a.warmup, a.layers)
+    cfg = r["cfg"]
+    M = cfg["M"]
+    nbytes = algorithmic_bytes(cfg, r["U"])
+    gbps = nbytes["total"] / (r["ms_step"] * 1e-3) / 1e9
+    # The decode path is one kernel (stage 0): its bytes are the step's
+    # algorithmic bytes and its duration the stage-0 event time.
+    kern_ms = float(r["stage_ms"][0]) if path != "grouped" else float(r["stage_ms"][3])
+    if path == "grouped":
+        fl = flops(cfg)
+        tfl = fl["gate_up"] / (kern_ms * 1e-3) / 1e12
+        roof = {"kernel": "gemm_kernel<routed gate/up>", "bound": "mfma",
+                "achieved": round(tfl, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tfl / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": fl["gate_up"], "avg_launch_us": round(kern_ms * 1e3, 3)}
+    else:
+        dom_gbps = nbytes["total"] / (kern_ms * 1e-3) / 1e9
+        roof = {"kernel": "decode_kernel", "bound": "hbm", "achieved": round(dom_gbps, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+                "traffic": None, "bytes_per_launch": nbytes["total"],
+                "avg_launch_us": round(kern_ms * 1e3, 3)}
     res = {
-        "metric": "MoE-layer tokens/sec at M=8 decode; achieved HBM GB/s vs peak",
-        "value": round(value, 1),
+        "metric": METRIC,
+        "value": round(M / (r["ms_step"] * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": round(r["ms_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if not nvfp4 else "bf16 x nvfp4 (fp32 accumulate)",
+        "dtype": "bf16 x nvfp4 (fp32 accumulate)" if cfg["experts"] == "nvfp4" else "bf16",
         "data": "synthetic (seeded; random weights of the Flint MoE shapes)",
-        "config": {"workload": cfg["name"], "M": M, "H": H, "E": E, "I": I, "SI": SI,
-                   "top_k": k, "experts": cfg["experts"], "touched_experts": U,
-                   "layers_rotated": L, "weights_bytes_per_layer": per_layer},
+        "config": {"workload": cfg["name"], "M": M, "H": cfg["H"], "E": cfg["E"], "I": cfg["I"],
+                   "SI": cfg["SI"], "top_k": cfg["top_k"], "experts": cfg["experts"],
+                   "touched_experts": r["U"], "layers_rotated": r["L"],
+                   "weights_bytes_per_layer": r["per_layer"]},
         "hbm_gbps": round(gbps, 1),
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": nbytes["total"],
-        "roofline": {"kernel": dom_name, "bound": "hbm", "achieved": round(dom_gbps, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "bytes_per_launch": dom_bytes,
-                     "avg_launch_us": round(kern_ms * 1e3, 3)},
+        "roofline": roof,
     }
+    if path == "grouped":
+        res["stage_us"] = {n: round(float(t) * 1e3, 2) for n, t in zip(fm.STAGES, r["stage_ms"])}
     if not a.no_cpu_baseline:
+        inp = synth.make_inputs(cfg_idx)
         res["cpu_baseline"] = cpu_baseline(inp, a.cpu_seconds)
+        del inp
+    if not a.no_grouped and path != "grouped":
+        g = run(fm, synth, torch, 4, "grouped", a.grouped_steps, 3, 1)
+        gc = g["cfg"]
+        fl = flops(gc)
+        st = g["stage_ms"]
+        gemm_ms = {"gate_up": st[3], "down": st[4], "shared_gate_up": st[2],
+                   "shared_down": st[5]}
+        res["grouped"] = {
+            "workload": gc["name"], "M": gc["M"], "steps": a.grouped_steps,
+            "ms_per_step": round(g["ms_step"], 4),
+            "tokens_per_s": round(gc["M"] / (g["ms_step"] * 1e-3), 1),
+            "tflops_per_s": round(fl["total"] / (g["ms_step"] * 1e-3) / 1e12, 1),
+            "mfma_frac": round(fl["total"] / (g["ms_step"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "stage_us": {n: round(float(t) * 1e3, 2) for n, t in zip(fm.STAGES, st)},
+            "gemm_tflops": {n: round(fl[n] / (gemm_ms[n] * 1e-3) / 1e12, 1) for n in gemm_ms},
+            "roofline": {"kernel": "gemm_kernel<routed gate/up>", "bound": "mfma",
+                         "achieved": round(fl["gate_up"] / (st[3] * 1e-3) / 1e12, 1),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(fl["gate_up"] / (st[3] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                         "flops_per_launch": fl["gate_up"], "avg_launch_us": round(st[3] * 1e3, 2)},
+        }
     print(json.dumps(res), flush=True)
 
 

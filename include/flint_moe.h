@@ -101,14 +101,15 @@ typedef struct {
   /* Stage timing: NULL, or an array of FLINT_STAGE_EVENTS hipEvent_t
    * (caller-created).  events[i] is recorded on `stream` just before stage i
    * is queued and events[FLINT_STAGE_EVENTS - 1] after the last stage, so
-   * hipEventElapsedTime(events[i], events[i + 1]) times stage i.  Stages:
-   * 0 routing, 1 routed gate/up, 2 shared gate/up, 3 routed down,
-   * 4 shared down, 5 combine (absent stages take no time).  The decode
-   * entry points record them; others ignore the field. */
+   * hipEventElapsedTime(events[i], events[i + 1]) times stage i.  Stages of
+   * flint_moe_grouped: 0 router GEMM and top-k, 1 expert pair lists,
+   * 2 shared gate/up, 3 routed gate/up, 4 routed down, 5 shared down,
+   * 6 combine.  The decode entry points run one kernel: it is stage 0 and
+   * the other stages take no time. */
   void **stage_events;
 } flint_moe_debug;
 
-#define FLINT_STAGE_EVENTS 7
+#define FLINT_STAGE_EVENTS 8
 
 /* Status code -> static string. */
 const char *flint_status_str(int status);

@@ -57,8 +57,8 @@ class SharedExpert(ctypes.Structure):
     _fields_ = [("w_gu", P), ("w_down", P), ("SI", I32)]
 
 
-FLINT_STAGE_EVENTS = 7
-STAGES = ("route", "gate_up", "shared_gate_up", "down", "shared_down", "combine")
+FLINT_STAGE_EVENTS = 8
+STAGES = ("route", "pair_lists", "shared_gate_up", "gate_up", "down", "shared_down", "combine")
 
 
 class MoeDebug(ctypes.Structure):

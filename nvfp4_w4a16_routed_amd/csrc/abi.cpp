@@ -52,6 +52,8 @@ Workspace carve_workspace(void *base, int M, int H, int E, int I, int SI, int to
   w.y = static_cast<uint16_t *>(take(2 * P * H));
   w.sact = static_cast<uint16_t *>(take(2 * (size_t)M * (SI > 0 ? SI : 0)));
   w.sh = static_cast<uint16_t *>(take(2 * (size_t)M * H));
+  w.lists = static_cast<int32_t *>(take(4 * (size_t)E * M));
+  w.counts = static_cast<int32_t *>(take(4 * (size_t)E));
   w.bytes = off;
   return w;
 }
@@ -105,8 +107,8 @@ int run_decode(int fmt, const uint16_t *x, const uint16_t *router, const void *w
   uint16_t *sact = (dbg && dbg->sact_out) ? dbg->sact_out : W.sact;
   uint16_t *sh = (dbg && dbg->sh_out) ? dbg->sh_out : W.sh;
   void **ev = dbg ? dbg->stage_events : nullptr;
-  auto mark = [&](int i) {
-    if (ev && ev[i]) hipEventRecord((hipEvent_t)ev[i], st);
+  auto mark = [&](int i) -> hipError_t {
+    return (ev && ev[i]) ? hipEventRecord((hipEvent_t)ev[i], st) : hipSuccess;
   };
   DecodeArgs a{};
   a.x = x;
@@ -137,9 +139,9 @@ int run_decode(int fmt, const uint16_t *x, const uint16_t *router, const void *w
   a.I = I;
   a.top_k = top_k;
   // One kernel runs every stage: the stage events bracket the whole of it.
-  mark(0);
-  hipError_t e = launch_decode(fmt, a, st);
-  for (int i = 1; i < FLINT_STAGE_EVENTS; ++i) mark(i);
+  hipError_t e = mark(0);
+  if (e == hipSuccess) e = launch_decode(fmt, a, st);
+  for (int i = 1; i < FLINT_STAGE_EVENTS && e == hipSuccess; ++i) e = mark(i);
   return hip_status(e);
 }
 
@@ -261,9 +263,74 @@ int flint_moe_grouped(const uint16_t *x, const uint16_t *router, const flint_nvf
                       const flint_shared_expert *shared, int M, int H, int E, int I, int top_k,
                       uint16_t *out, const flint_moe_debug *dbg, void *ws, size_t ws_bytes,
                       void *stream) {
-  (void)x; (void)router; (void)w; (void)shared; (void)M; (void)H; (void)E; (void)I;
-  (void)top_k; (void)out; (void)dbg; (void)ws; (void)ws_bytes; (void)stream;
-  return FLINT_ERR_SHAPE;
+  const bool forced = dbg && dbg->ids_in;
+  const bool has_shared = shared && shared->w_gu;
+  const int SI = has_shared ? shared->SI : 0;
+  if (M < 0 || top_k < 1 || E < 1 || top_k > E || E > kMaxExperts) return FLINT_ERR_SHAPE;
+  if ((long)M * top_k > (long)1 << 30) return FLINT_ERR_SHAPE;
+  if (!grouped_shape_supported(H, I, SI)) return FLINT_ERR_SHAPE;
+  if (M == 0) return FLINT_OK;  // nothing to compute; no pointer is used
+  if (!x || !w || !out || (!forced && !router)) return FLINT_ERR_NULL;
+  if (!w->w13 || !w->s13 || !w->a13 || !w->w2 || !w->s2 || !w->a2) return FLINT_ERR_NULL;
+  if (forced && !dbg->tw_in) return FLINT_ERR_NULL;
+  if (has_shared && !shared->w_down) return FLINT_ERR_NULL;
+  if (!ws) return FLINT_ERR_WORKSPACE;
+  if (!aligned16(x) || (router && !aligned16(router)) || !aligned16(out) || !aligned16(ws) ||
+      !aligned16(w->w13) || !aligned16(w->s13) || !aligned16(w->a13) || !aligned16(w->w2) ||
+      !aligned16(w->s2) || !aligned16(w->a2) ||
+      (has_shared && (!aligned16(shared->w_gu) || !aligned16(shared->w_down))))
+    return FLINT_ERR_ALIGN;
+  Workspace W = carve_workspace(ws, M, H, E, I, SI, top_k);
+  if (W.bytes > ws_bytes) return FLINT_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  GroupedArgs a{};
+  a.x = x;
+  a.router = router;
+  a.w13 = w->w13;
+  a.s13 = w->s13;
+  a.a13 = w->a13;
+  a.w2 = w->w2;
+  a.s2 = w->s2;
+  a.a2 = w->a2;
+  a.sgu = has_shared ? shared->w_gu : nullptr;
+  a.sdown = has_shared ? shared->w_down : nullptr;
+  a.ids_in = forced ? dbg->ids_in : nullptr;
+  a.logits = (dbg && dbg->logits_out) ? dbg->logits_out : W.logits;
+  int32_t *ids = (dbg && dbg->ids_out) ? dbg->ids_out : W.ids;
+  float *tw = (dbg && dbg->tw_out) ? dbg->tw_out : W.tw;
+  if (forced) {
+    // the given routing, copied where the outputs were asked for
+    const size_t P = (size_t)M * top_k;
+    if (dbg->ids_out) {
+      hipError_t e = hipMemcpyAsync(ids, dbg->ids_in, 4 * P, hipMemcpyDeviceToDevice, st);
+      if (e != hipSuccess) return hip_status(e);
+    } else {
+      ids = const_cast<int32_t *>(dbg->ids_in);
+    }
+    if (dbg->tw_out) {
+      hipError_t e = hipMemcpyAsync(tw, dbg->tw_in, 4 * P, hipMemcpyDeviceToDevice, st);
+      if (e != hipSuccess) return hip_status(e);
+    } else {
+      tw = const_cast<float *>(dbg->tw_in);
+    }
+  }
+  a.ids = ids;
+  a.tw = tw;
+  a.lists = W.lists;
+  a.counts = W.counts;
+  a.act = (dbg && dbg->act_out) ? dbg->act_out : W.act;
+  a.y = (dbg && dbg->y_out) ? dbg->y_out : W.y;
+  a.sact = (dbg && dbg->sact_out) ? dbg->sact_out : W.sact;
+  a.sh = (dbg && dbg->sh_out) ? dbg->sh_out : W.sh;
+  a.out = out;
+  a.events = dbg ? dbg->stage_events : nullptr;
+  a.M = M;
+  a.H = H;
+  a.E = E;
+  a.I = I;
+  a.SI = SI;
+  a.top_k = top_k;
+  return hip_status(launch_grouped(a, st));
 }
 
 }  // extern "C"

@@ -1,3 +1,576 @@
-// Grouped (prefill) path: MFMA kernels, added next.
+// The MoE block for prefill-size batches: grouped GEMMs on the matrix cores.
+//
+// Semantics (vLLM page "vllm.models.flint.ops.moe": module docstring
+// "Numerics", the grouped branch of flint_moe and _combine_kernel):
+//   logits = bf16(fp32 x . router^T);  top-k and weights as in decode
+//   per expert e, for its pairs p = t * top_k + j (ascending):
+//     g, u = fp32 (x[t] . W13[e, n]) * alpha13[e], (x[t] . W13[e, I + n]) * ...
+//     act[p, n] = bf16(silu(g) * u)
+//     y[p, h]   = bf16(fp32 (act[p] . W2[e, h]) * alpha2[e])
+//   shared: sact = bf16(silu(xWg) * xWu), sh = bf16(sact . Wd)   (fp32 sums)
+//   out[t, h] = bf16(bf16(sum_j tw[t, j] y[t*k + j, h]) + sh[t, h])
+//
+// One GEMM kernel, C[rows, cols] = A[rows, K] . B[cols, K]^T, serves every
+// product: the router, the shared expert's gate/up and down, and the routed
+// experts' gate/up and down with A rows gathered through each expert's pair
+// list.  NVFP4 B tiles are dequantised exactly (E2M1 value times its E4M3
+// block scale, in fp32, then to bf16) into LDS; every product is a bf16 MFMA
+// (v_mfma_f32_32x32x16_bf16) with fp32 accumulation.  Epilogues apply the
+// rule: global scale, SwiGLU, bf16 rounding; a memory-bound kernel then
+// forms the weighted combine and the shared add.
+//
+// Tile: 256 rows x 128 columns, K steps of 32; 4 waves, wave w owns rows
+// [64 w, 64 w + 64) and all 128 columns (2 x 4 MFMA tiles of 32 x 32).
+// Tiles go global -> registers (two K steps ahead) -> LDS (two stages, NVFP4
+// B dequantised on the way), with the 16-byte chunks of each 64-byte LDS row
+// XOR-swizzled so the accesses are spread over the LDS banks.
 #include "common.hpp"
 #include "internal.hpp"
+
+namespace flint {
+
+namespace {
+
+constexpr int kGThreads = 256;
+constexpr int kBM = 256;  // tile rows (pairs or tokens)
+constexpr int kBN = 128;  // tile columns (B rows)
+constexpr int kBK = 32;   // K per step (4 chunks of 8 bf16)
+constexpr int kStages = 2;  // LDS stages; register loads run two K steps ahead
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+enum GemmMode {
+  kRouter = 0,       // logits[t, c] = bf16(x[t] . R[c])
+  kSharedGateUp = 1, // sact[t, n] = bf16(swiglu(x[t] . Wg[n], x[t] . Wu[n]))
+  kSharedDown = 2,   // sh[t, h] = bf16(sact[t] . Wd[h])
+  kRoutedGateUp = 3, // act[p, n] = bf16(swiglu(a13 x[t(p)] . W13[n], a13 x[t(p)] . W13[I+n]))
+  kRoutedDown = 4    // y[p, h] = bf16(a2 * act[p] . W2[h])
+};
+
+struct GemmArgs {
+  const uint16_t *a;     // A source rows (x, sact or act), row length K
+  const uint8_t *b;      // B: bf16 rows, or NVFP4 codes
+  const uint8_t *bs;     // NVFP4 scales (else NULL)
+  const float *alpha;    // NVFP4 global scales [E] (else NULL)
+  uint16_t *c;           // output rows
+  int rows;              // dense modes: number of A rows (tokens)
+  int a_rows;            // rows of the A matrix (its extent for the loads)
+  int K;                 // reduction length
+  int ncols;             // output columns (B rows; for gate/up: act columns)
+  int ldc;               // output row length
+  int I;                 // gate/up: offset of the up rows in B
+  int top_k;
+  // routed modes: expert pair lists
+  const int32_t *lists;  // [E][list_stride] pair indices, ascending
+  const int32_t *counts; // [E]
+  int list_stride, E;
+};
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Buffer descriptor of `bytes` bytes at p (raw, untyped; word 3 as the
+// gfx9-family raw buffer loads expect).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, size_t bytes) {
+  const int n = bytes > 0x7fffffffu ? 0x7fffffff : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, n, 0x00020000);
+}
+__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+
+// LDS position (in 16-byte chunks) of chunk c of tile row r.  The XOR
+// pattern keeps both kinds of access free of bank conflicts: an MFMA operand
+// read (16 lanes a cycle: 16 consecutive rows, one chunk each, a 256-byte
+// bank window) and a dequantised-B store (8 lanes a cycle: 4 rows, chunks
+// 2h + i of lanes (r, h), a 128-byte window).
+__device__ __forceinline__ int swz_x(int r) { return ((r >> 2) & 3) ^ ((r >> 1) & 1); }
+__device__ __forceinline__ int swz(int r, int c) { return r * 4 + (c ^ swz_x(r)); }
+
+// E2M1 codes (8 per dword) times one E4M3 scale -> 8 exact bf16 values.
+// The hardware converter applies only the exponent of its scale operand, so
+// it converts with scale 1 and the fp32 product with the scale is formed
+// explicitly; it has at most 6 significant bits, so truncating it to bf16
+// is exact.
+template <int SEL>
+__device__ __forceinline__ uint32_t dequant2(uint32_t codes, float scale) {
+  typedef __attribute__((ext_vector_type(2))) float f2;
+  const f2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, SEL);
+  const uint32_t lo = __float_as_uint(v[0] * scale), hi = __float_as_uint(v[1] * scale);
+  return __builtin_amdgcn_perm(hi, lo, 0x07060302u);  // high halves: {lo.bf16, hi.bf16}
+}
+__device__ __forceinline__ u32x4_t dequant8(uint32_t codes, float scale) {
+  return u32x4_t{dequant2<0>(codes, scale), dequant2<1>(codes, scale), dequant2<2>(codes, scale),
+                 dequant2<3>(codes, scale)};
+}
+
+template <int MODE>
+struct ModeInfo {
+  static constexpr bool kRouted = MODE == kRoutedGateUp || MODE == kRoutedDown;
+  static constexpr bool kGateUp = MODE == kSharedGateUp || MODE == kRoutedGateUp;
+  static constexpr bool kNvfp4 = kRouted;
+};
+
+template <int MODE>
+__global__ void __launch_bounds__(kGThreads, 2) gemm_kernel(GemmArgs g) {
+  using MI = ModeInfo<MODE>;
+  __shared__ __attribute__((aligned(16))) uint16_t As[kStages][kBM * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[kStages][kBN * kBK];
+  __shared__ int rowidx[kBM];  // A row (token or pair) of each tile row, -1 = none
+  __shared__ int outrow[kBM];  // output row of each tile row
+  __shared__ int tile_info[4];
+
+  const int lane = lane_id(), wv = wave_id();
+  const int ntn = MI::kGateUp ? g.ncols / (kBN / 2) : (g.ncols + kBN - 1) / kBN;  // column tiles
+  // Tile of this block.  Blocks are dealt to the XCDs round-robin; the
+  // column tiles of one row tile are given to consecutive blocks of one XCD
+  // so its A rows are reused from that XCD's L2.
+  const int nblk = gridDim.x;
+  const int xcd = blockIdx.x % 8, per = nblk / 8;
+  const int b = blockIdx.x < per * 8 ? xcd * per + blockIdx.x / 8 : blockIdx.x;
+  const int mt = b / ntn, nt = b % ntn;
+  if constexpr (MI::kRouted) {
+    // row tiles of expert e: ceil(count / 256), rows split evenly over them
+    for (int i = threadIdx.x; i < g.E; i += kGThreads) rowidx[i] = g.counts[i];
+    __syncthreads();
+    if (wv == 0) {
+      int nt4[4], c4[4], tot = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ee = 4 * lane + i;
+        c4[i] = ee < g.E ? rowidx[ee] : 0;
+        nt4[i] = (c4[i] + kBM - 1) / kBM;
+        tot += nt4[i];
+      }
+      int acc = tot;  // exclusive prefix over lanes
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int t = __shfl_up(acc, o, kWave);
+        if (lane >= o) acc += t;
+      }
+      acc -= tot;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (mt >= acc && mt < acc + nt4[i]) {
+          const int q = mt - acc, c = c4[i], ntile = nt4[i];
+          const int per_t = ((c + ntile - 1) / ntile + 31) / 32 * 32;
+          tile_info[0] = 4 * lane + i;
+          tile_info[1] = q * per_t;
+          tile_info[2] = min(per_t, c - q * per_t);
+        }
+        acc += nt4[i];
+      }
+      if (lane == kWave - 1 && mt >= acc) tile_info[0] = -1;  // beyond the last tile
+    }
+  } else if (threadIdx.x == 0) {
+    tile_info[0] = 0;
+    tile_info[1] = mt * kBM;
+    tile_info[2] = min(kBM, g.rows - mt * kBM);
+  }
+  __syncthreads();
+  const int e = tile_info[0], m0 = tile_info[1], nrows = tile_info[2];
+  if (e < 0 || nrows <= 0) return;
+  const int n0 = nt * (MI::kGateUp ? kBN / 2 : kBN);
+
+  // Row indices of the tile; rows past the end repeat the first row (their
+  // loads stay in bounds and their results are dropped).
+  for (int i = threadIdx.x; i < kBM; i += kGThreads) {
+    const int ii = i < nrows ? i : 0;
+    int src, dst;
+    if constexpr (MI::kRouted) {
+      const int p = g.lists[(size_t)e * g.list_stride + m0 + ii];
+      dst = p;
+      src = MODE == kRoutedGateUp ? p / g.top_k : p;
+    } else {
+      src = dst = m0 + ii;
+    }
+    rowidx[i] = src;
+    outrow[i] = i < nrows ? dst : -1;
+  }
+  __syncthreads();
+
+  const int K = g.K;
+  const int nk = K / kBK;
+  // B row of tile column r
+  auto brow = [&](int r) -> int {
+    if constexpr (MI::kGateUp) return r < kBN / 2 ? n0 + r : g.I + n0 + (r - kBN / 2);
+    else return n0 + r;
+  };
+  const int ncols_b = MI::kGateUp ? 2 * g.I : g.ncols;  // valid B rows
+  const size_t bexp_rows = (size_t)e * ncols_b;          // expert offset in rows (routed)
+
+  // ---- loaders.  Each K step moves 256 x 32 A values and 128 x 32 B
+  // values (as 16-byte chunks) global -> registers -> LDS.  Thread slot
+  // s = (u * 4 + wave) * 64 + lane (u < 4 for A, u < 2 for B) owns LDS chunk
+  // s, i.e. row s / 4 and stored chunk s % 4, which holds logical chunk
+  // (s % 4) ^ swz_x(row): a wave's LDS stores are 1 KB contiguous and its
+  // global loads read whole 64-byte row segments.  The rows a thread loads
+  // never change, so their addresses are formed once.
+  // Loads are buffer loads: a descriptor per operand (uniform), a fixed
+  // per-thread byte offset (one VGPR) and the K step's offset in a scalar
+  // register, so no vector register is spent forming addresses; reads past
+  // a descriptor's size return zero instead of touching other memory.
+  uint32_t a_off[4];
+  int a_slot[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int sl = (u * 4 + wv) * kWave + lane;
+    const int r = sl >> 2, c = (sl & 3) ^ swz_x(r);
+    a_off[u] = (uint32_t)(((size_t)rowidx[r] * K + c * 8) * 2);
+    a_slot[u] = sl;
+  }
+  uint32_t b_off[2];
+  int b_slot[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int sl = (u * 4 + wv) * kWave + lane;
+    const int r = sl >> 2, c = (sl & 3) ^ swz_x(r);
+    const int br = brow(r) < ncols_b ? brow(r) : 0;  // columns past the end: dropped
+    b_off[u] = MI::kNvfp4 ? 0u : (uint32_t)(((size_t)br * K + c * 8) * 2);
+    b_slot[u] = sl;
+  }
+  // NVFP4 B: thread t dequantises 16 elements of row t / 2 (half t % 2)
+  const int br_t = threadIdx.x >> 1, bh_t = threadIdx.x & 1;
+  const uint32_t bc_off = (uint32_t)(brow(br_t) * (K / 2) + bh_t * 8);
+  const uint32_t bs_off = (uint32_t)(brow(br_t) * (K / 16) + bh_t);
+  const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(g.a, (size_t)g.a_rows * K * 2);
+  const __amdgpu_buffer_rsrc_t rs_b =
+      MI::kNvfp4 ? make_rsrc(g.b + bexp_rows * (K / 2), (size_t)ncols_b * (K / 2))
+                 : make_rsrc(g.b, (size_t)ncols_b * K * 2);
+  const __amdgpu_buffer_rsrc_t rs_s =
+      make_rsrc(MI::kNvfp4 ? g.bs + bexp_rows * (K / 16) : g.b, MI::kNvfp4 ? (size_t)ncols_b * (K / 16) : 0);
+
+  struct Regs {
+    u32x4_t a[4];
+    u32x4_t b[2];     // bf16 B
+    uint2 codes;      // NVFP4 B
+    uint32_t scale;
+  };
+  auto load = [&](Regs &R, int kb) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      R.a[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_a, a_off[u], kb * kBK * 2, 0));
+    if constexpr (MI::kNvfp4) {
+      R.codes = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs_b, bc_off, kb * (kBK / 2), 0));
+      R.scale = __builtin_amdgcn_raw_buffer_load_b8(rs_s, bs_off, kb * 2, 0);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        R.b[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_b, b_off[u], kb * kBK * 2, 0));
+    }
+  };
+  auto store = [&](int stage, const Regs &R) {
+    u32x4_t *as = reinterpret_cast<u32x4_t *>(&As[stage][0]);
+    u32x4_t *bs = reinterpret_cast<u32x4_t *>(&Bs[stage][0]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) as[a_slot[u]] = R.a[u];
+    if constexpr (MI::kNvfp4) {
+      const float sc = e4m3_to_f32(R.scale);
+      bs[swz(br_t, 2 * bh_t)] = dequant8(R.codes.x, sc);
+      bs[swz(br_t, 2 * bh_t + 1)] = dequant8(R.codes.y, sc);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) bs[b_slot[u]] = R.b[u];
+    }
+  };
+
+  f32x16_t acc[2][4];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.0f;
+  const bool mact0 = 64 * wv < nrows, mact1 = 64 * wv + 32 < nrows;
+
+  // One K step kb on LDS stage kb % 2: loads of step kb + 2 into `next`
+  // (their latency spans two steps), MFMAs, then step kb + 1's registers
+  // (`held`, loaded one step ago) into the other stage, and a barrier.
+  auto step = [&](int kb, Regs &next, Regs &held) {
+    const int cur = kb & 1;
+    // Always issued (past the end: a repeat of the last step, never used),
+    // so the wait for `held` is "all but the loads just issued" on every path.
+    load(next, min(kb + 2, nk - 1));
+    const u32x4_t *Ac = reinterpret_cast<const u32x4_t *>(&As[cur][0]);
+    const u32x4_t *Bc = reinterpret_cast<const u32x4_t *>(&Bs[cur][0]);
+    // Every operand of the step is read first (one LDS round trip per step,
+    // not one per K half), then the two K halves of 16 run back to back.
+    u32x4_t av[2][2], bv[2][4];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int ch = 2 * sub + (lane >> 5);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) av[sub][m] = Ac[swz(64 * wv + 32 * m + (lane & 31), ch)];
+#pragma unroll
+      for (int n = 0; n < 4; ++n) bv[sub][n] = Bc[swz(32 * n + (lane & 31), ch)];
+    }
+    // (rows past the tile's end are computed too: the waves of a block run
+    // in step, and a branch per wave would only break up the schedule)
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+          acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av[sub][m]),
+                                                              __builtin_bit_cast(bf16x8_t, bv[sub][n]),
+                                                              acc[m][n], 0, 0, 0);
+      }
+    }
+    // Past the end this stores a repeat of the last step into the stage
+    // nobody reads again; unconditional, so the loop body has no branch.
+    store(cur ^ 1, held);
+    __syncthreads();
+  };
+
+  // ---- prologue: step 0 in LDS, step 1 in registers
+  Regs ra, rb;
+  if (nk > 0) {
+    load(ra, 0);
+    load(rb, min(1, nk - 1));
+    store(0, ra);
+  }
+  __syncthreads();
+  // nk is even: every K here (H, I, SI) is a multiple of 64.
+  for (int kb = 0; kb < nk; kb += 2) {
+    step(kb, ra, rb);      // loads step kb + 2 into ra, stores step kb + 1 from rb
+    step(kb + 1, rb, ra);  // loads step kb + 3 into rb, stores step kb + 2 from ra
+  }
+  __builtin_amdgcn_s_waitcnt(0x0070);  // the repeated loads of the last steps
+
+  // ---- epilogue: acc[m][n][r] is C[row, col], row = 64 wv + 32 m + 8 (r / 4)
+  // + 4 (lane / 32) + r % 4, col = 32 n + lane % 32.
+  const float alpha = MI::kNvfp4 ? g.alpha[e] : 1.0f;
+  const int cl = lane & 31;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    if (!(m == 0 ? mact0 : mact1)) continue;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 64 * wv + 32 * m + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (row >= nrows) continue;
+      const int orow = outrow[row];
+      if constexpr (MI::kGateUp) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          float gs = acc[m][n][r], us = acc[m][n + 2][r];
+          if constexpr (MI::kNvfp4) {
+            gs = gs * alpha;
+            us = us * alpha;
+          }
+          const int col = n0 + 32 * n + cl;
+          g.c[(size_t)orow * g.ldc + col] = (uint16_t)f32_to_bf16(swiglu(gs, us));
+        }
+      } else if constexpr (MODE == kRoutedDown) {
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+          g.c[(size_t)orow * g.ldc + n0 + 32 * n + cl] = (uint16_t)f32_to_bf16(acc[m][n][r] * alpha);
+      } else if constexpr (MODE == kRouter) {
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const int col = n0 + 32 * n + cl;
+          if (col < g.ncols) g.c[(size_t)orow * g.ldc + col] = (uint16_t)f32_to_bf16(acc[m][n][r]);
+        }
+      } else {  // kSharedDown
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+          g.c[(size_t)orow * g.ldc + n0 + 32 * n + cl] = (uint16_t)f32_to_bf16(acc[m][n][r]);
+      }
+    }
+  }
+}
+
+// out[t, h] = bf16(bf16(sum_j tw[t, j] y[t*k + j, h]) + sh[t, h]) for 8
+// consecutive h per thread: the k rows of y are loaded together (16 bytes
+// each), the sum is exact in fp64 (every product has 16 significant bits)
+// and rounded once to fp32.  sh == NULL: no shared expert.
+__global__ void __launch_bounds__(256) combine_kernel(const uint16_t *__restrict__ y,
+                                                      const float *__restrict__ tw,
+                                                      const int32_t *__restrict__ ids,
+                                                      const uint16_t *__restrict__ sh, int M, int H,
+                                                      int E, int k, uint16_t *__restrict__ out) {
+  const long gid = (long)blockIdx.x * 256 + threadIdx.x;
+  const int per_row = H / 8;
+  if (gid >= (long)M * per_row) return;
+  const int t = (int)(gid / per_row), h = (int)(gid % per_row) * 8;
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    u32x4_t v[8];
+    float w[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u;
+      const bool on = j < k && (unsigned)ids[(size_t)t * k + j] < (unsigned)E;
+      v[u] = on ? load16(y + ((size_t)t * k + j) * H + h) : u32x4_t{0, 0, 0, 0};
+      w[u] = on ? tw[(size_t)t * k + j] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        acc[2 * d] += (double)w[u] * (double)bf16_lo(v[u][d]);
+        acc[2 * d + 1] += (double)w[u] * (double)bf16_hi(v[u][d]);
+      }
+  }
+  const u32x4_t s = sh ? load16(sh + (size_t)t * H + h) : u32x4_t{0, 0, 0, 0};
+  u32x4_t o;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t lo = f32_to_bf16(round_bf16((float)acc[2 * d]) + bf16_lo(s[d]));
+    const uint32_t hi = f32_to_bf16(round_bf16((float)acc[2 * d + 1]) + bf16_hi(s[d]));
+    o[d] = lo | (hi << 16);
+  }
+  *reinterpret_cast<u32x4_t *>(out + (size_t)t * H + h) = o;
+}
+
+// Pair lists per expert: block e compacts the pairs p (ascending) whose
+// expert is e into lists[e][0 .. count), count into counts[e].
+__global__ void __launch_bounds__(256) plan_lists_kernel(const int32_t *__restrict__ ids, int npairs,
+                                                         int32_t *__restrict__ lists, int stride,
+                                                         int32_t *__restrict__ counts) {
+  __shared__ int wbase[4];
+  const int e = blockIdx.x;
+  const int lane = lane_id(), wv = wave_id();
+  int base = 0;
+  for (int p0 = 0; p0 < npairs; p0 += 256) {
+    const int p = p0 + threadIdx.x;
+    const bool hit = p < npairs && ids[p] == e;
+    const uint64_t m = __ballot(hit);
+    if (lane == 0) wbase[wv] = __popcll(m);
+    __syncthreads();
+    int off = base;
+    for (int w = 0; w < wv; ++w) off += wbase[w];
+    const int pos = off + __popcll(m & ((1ull << lane) - 1ull));
+    if (hit && pos < stride) lists[(size_t)e * stride + pos] = p;
+    const int tot = wbase[0] + wbase[1] + wbase[2] + wbase[3];
+    __syncthreads();
+    base += tot;
+  }
+  if (threadIdx.x == 0) counts[e] = min(base, stride);  // an expert has <= 1 pair per token
+}
+
+template <int MODE>
+hipError_t launch_gemm(const GemmArgs &g, int row_tiles, int col_tiles, hipStream_t st) {
+  const int nblk = row_tiles * col_tiles;
+  if (nblk <= 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_kernel<MODE>), dim3(nblk), dim3(kGThreads), 0, st, g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool grouped_shape_supported(int H, int I, int SI) {
+  return H % 128 == 0 && I % 64 == 0 && H >= 128 && I >= 64 && H <= 8192 && I <= 8192 &&
+         (SI == 0 || (SI % 64 == 0 && SI <= 8192));
+}
+
+hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
+  const int M = a.M, H = a.H, E = a.E, I = a.I, k = a.top_k, SI = a.SI;
+  const int P = M * k;
+  hipError_t err;
+  auto mark = [&](int i) -> hipError_t {
+    return (a.events && a.events[i]) ? hipEventRecord((hipEvent_t)a.events[i], st) : hipSuccess;
+  };
+  // 1. router logits and top-k (skipped with forced routing)
+  if ((err = mark(0)) != hipSuccess) return err;
+  if (!a.ids_in) {
+    GemmArgs r{};
+    r.a = a.x;
+    r.b = reinterpret_cast<const uint8_t *>(a.router);
+    r.c = a.logits;
+    r.rows = M;
+    r.a_rows = M;
+    r.K = H;
+    r.ncols = E;
+    r.ldc = E;
+    if ((err = launch_gemm<kRouter>(r, (M + kBM - 1) / kBM, (E + kBN - 1) / kBN, st)) != hipSuccess)
+      return err;
+    if ((err = launch_topk(a.logits, M, E, k, a.ids, a.tw, nullptr, st)) != hipSuccess) return err;
+  }
+  // 2. pair lists per expert
+  if ((err = mark(1)) != hipSuccess) return err;
+  hipLaunchKernelGGL(plan_lists_kernel, dim3(E), dim3(256), 0, st, a.ids, P, a.lists, M, a.counts);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  // 3. shared gate/up
+  if ((err = mark(2)) != hipSuccess) return err;
+  if (a.sgu) {
+    GemmArgs s{};
+    s.a = a.x;
+    s.b = reinterpret_cast<const uint8_t *>(a.sgu);
+    s.c = a.sact;
+    s.rows = M;
+    s.a_rows = M;
+    s.K = H;
+    s.ncols = SI;
+    s.ldc = SI;
+    s.I = SI;
+    if ((err = launch_gemm<kSharedGateUp>(s, (M + kBM - 1) / kBM, SI / (kBN / 2), st)) != hipSuccess)
+      return err;
+  }
+  // 4. routed gate/up: row tiles bounded by sum_e ceil(count_e / 256)
+  if ((err = mark(3)) != hipSuccess) return err;
+  const int max_row_tiles = (P + kBM - 1) / kBM + E;
+  {
+    GemmArgs gu{};
+    gu.a = a.x;
+    gu.a_rows = M;
+    gu.b = a.w13;
+    gu.bs = a.s13;
+    gu.alpha = a.a13;
+    gu.c = a.act;
+    gu.K = H;
+    gu.ncols = I;
+    gu.ldc = I;
+    gu.I = I;
+    gu.top_k = k;
+    gu.lists = a.lists;
+    gu.counts = a.counts;
+    gu.list_stride = M;
+    gu.E = E;
+    if ((err = launch_gemm<kRoutedGateUp>(gu, max_row_tiles, I / (kBN / 2), st)) != hipSuccess)
+      return err;
+  }
+  // 5. routed down
+  if ((err = mark(4)) != hipSuccess) return err;
+  {
+    GemmArgs dn{};
+    dn.a = a.act;
+    dn.a_rows = P;
+    dn.b = a.w2;
+    dn.bs = a.s2;
+    dn.alpha = a.a2;
+    dn.c = a.y;
+    dn.K = I;
+    dn.ncols = H;
+    dn.ldc = H;
+    dn.top_k = k;
+    dn.lists = a.lists;
+    dn.counts = a.counts;
+    dn.list_stride = M;
+    dn.E = E;
+    if ((err = launch_gemm<kRoutedDown>(dn, max_row_tiles, H / kBN, st)) != hipSuccess) return err;
+  }
+  // 6. shared down -> sh
+  if ((err = mark(5)) != hipSuccess) return err;
+  if (a.sgu) {
+    GemmArgs sd{};
+    sd.a = a.sact;
+    sd.b = reinterpret_cast<const uint8_t *>(a.sdown);
+    sd.c = a.sh;
+    sd.rows = M;
+    sd.a_rows = M;
+    sd.K = SI;
+    sd.ncols = H;
+    sd.ldc = H;
+    if ((err = launch_gemm<kSharedDown>(sd, (M + kBM - 1) / kBM, H / kBN, st)) != hipSuccess) return err;
+  }
+  // 7. combine + shared add
+  if ((err = mark(6)) != hipSuccess) return err;
+  {
+    const long n = (long)M * (H / 8);
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.y, a.tw,
+                       a.ids, a.sgu ? a.sh : nullptr, M, H, E, k, a.out);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  return mark(7);
+}
+
+}  // namespace flint

@@ -82,6 +82,8 @@ struct Workspace {
   uint16_t *y;         // [M*k, H]
   uint16_t *sact;      // [M, SI]
   uint16_t *sh;        // [M, H]
+  int32_t *lists;      // [E, M] grouped pair lists
+  int32_t *counts;     // [E]
   size_t bytes;        // total bytes used
 };
 
@@ -111,5 +113,30 @@ hipError_t launch_decode(int fmt, const DecodeArgs &a, hipStream_t st);
 
 // Whether the decode kernel is compiled for this (H, I) (both formats).
 bool decode_shape_supported(int H, int I);
+
+// Arguments of the grouped (prefill) path: device pointers, caller-owned.
+struct GroupedArgs {
+  const uint16_t *x, *router;
+  const uint8_t *w13, *s13;
+  const float *a13;
+  const uint8_t *w2, *s2;
+  const float *a2;
+  const uint16_t *sgu, *sdown;  // shared expert (bf16), NULL = none
+  const int32_t *ids_in;        // forced routing, NULL = route
+  uint16_t *logits;             // [M, E]
+  int32_t *ids;                 // [M, k] (ids_in when forced)
+  float *tw;                    // [M, k]
+  int32_t *lists;               // [E, M] pair lists
+  int32_t *counts;              // [E]
+  uint16_t *act, *y, *sact, *sh, *out;
+  void **events;                // NULL, or 8 hipEvent_t: recorded before each stage and at the end
+  int M, H, E, I, SI, top_k;
+};
+
+// The MoE block with grouped MFMA GEMMs (any M >= 1).
+hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st);
+
+// Whether the grouped kernels handle these sizes.
+bool grouped_shape_supported(int H, int I, int SI);
 
 }  // namespace flint

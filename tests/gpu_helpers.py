@@ -136,6 +136,17 @@ def check_y(gpu_y, ref_y, det, label=""):
     return float(np.mean(err > 0))
 
 
+def check_logits(gpu_lg, ref_lg, x, router, label=""):
+    """Router logits within one bf16 ulp plus the bound of an fp32 sum in any
+    order (GAMMA * sum |x_h R_eh|)."""
+    mag = np.abs(bf(x)) @ np.abs(bf(router)).T
+    tol = ulp_bf16(bf(ref_lg)) + GAMMA * mag
+    err = np.abs(bf(gpu_lg) - bf(ref_lg))
+    bad = err > tol
+    assert not bad.any(), (f"{label} logits: {bad.sum()} beyond tolerance; worst err/tol "
+                           f"{np.max(err / tol):.3g}")
+
+
 def end_to_end_ulps(out_gpu, ref: dict, k: int, rows=None):
     """|out_gpu - out_ref| in units of ulp_bf16(m) per element, over `rows`
     (a boolean token mask; default all tokens)."""
@@ -149,3 +160,51 @@ def end_to_end_ulps(out_gpu, ref: dict, k: int, rows=None):
     m = np.maximum.reduce([np.abs(out_r), np.abs(routed), np.abs(sh),
                            np.max(np.abs(tw * y), axis=1)])
     return np.abs(bf(np.asarray(out_gpu)[rows]) - out_r) / ulp_bf16(m)
+
+
+def same_f32(a, b) -> bool:
+    """Bitwise equality of float32 arrays (NaN == NaN)."""
+    a, b = np.asarray(a, np.float32), np.asarray(b, np.float32)
+    return np.array_equal(np.isnan(a), np.isnan(b)) and np.array_equal(
+        a[~np.isnan(a)].view(np.uint32), b[~np.isnan(b)].view(np.uint32))
+
+
+def stagewise(inp, r, say=print):
+    """Checks every stage of a GPU run against the oracle fed with the GPU's
+    own upstream values; returns the oracle's end-to-end result."""
+    cfg = inp["cfg"]
+    k, I, H = cfg["top_k"], cfg["I"], cfg["H"]
+    label = cfg["name"]
+    # routing: ids / tw bit-exact given the GPU's logits
+    ref_lg = oracle.logits(inp["x"], inp["router"])
+    check_logits(r["logits"], ref_lg, inp["x"], inp["router"], label)
+    rids, rtw, _ = oracle.topk(r["logits"], k)
+    assert np.array_equal(r["ids"], rids) and same_f32(r["tw"], rtw)
+    # gate/up on the GPU's routing
+    act, det = oracle.gate_up(inp["x"], r["ids"], k, inp, I, want_detail=True)
+    check_act(r["act"], act, det, label)
+    # down on the GPU's act
+    y, ydet = oracle.down(r["act"], r["ids"], inp, H, want_detail=True)
+    check_y(r["y"], y, ydet, label)
+    sh = None
+    if "sgu" in inp:
+        sact, sh_ref, sdet = oracle.shared_expert(inp["x"], inp["sgu"], inp["sdown"], True)
+        check_act(r["sact"], sact, sdet["gate_up"], label + " shared")
+        zeros = np.zeros(cfg["M"], np.int32)
+        sh2, shdet = oracle.down(r["sact"], zeros, dict(bw2=inp["sdown"][None]), H, True)
+        check_y(r["sh"], sh2, shdet, label + " shared")
+        sh = r["sh"]
+    # combine: bit-exact on the GPU's y, tw and shared output
+    out_c, _ = oracle.combine(r["y"], r["tw"], sh, k)
+    assert np.array_equal(r["out"], out_c), "combine differs"
+    # end to end against the oracle's own routing
+    full = oracle.moe_block(inp)
+    same = np.all(full["ids"] == r["ids"], axis=1)
+    ulps = end_to_end_ulps(r["out"], full, k, rows=same)
+    say(f"{label}: tokens {cfg['M']}, near-tie flips {int((~same).sum())}, "
+         f"max ulp(m) {ulps.max() if ulps.size else 0:.3f}, "
+         f"mean nonzero {np.mean(ulps > 0) if ulps.size else 0:.4f}")
+    assert ulps.size == 0 or ulps.max() <= 2.0
+    return full
+
+

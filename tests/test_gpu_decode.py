@@ -133,45 +133,6 @@ def test_route_logits_and_topk(M, E, H):
 
 # -------------------------------------------------------- decode blocks
 
-def _stagewise(inp, r, path):
-    """Checks every stage of a GPU run against the oracle fed with the GPU's
-    own upstream values; returns the oracle's end-to-end result."""
-    cfg = inp["cfg"]
-    k, I, H = cfg["top_k"], cfg["I"], cfg["H"]
-    label = cfg["name"]
-    # routing: ids / tw bit-exact given the GPU's logits
-    ref_lg = oracle.logits(inp["x"], inp["router"])
-    assert np.all(np.abs(G.bf(r["logits"]) - G.bf(ref_lg)) <= G.ulp_bf16(G.bf(ref_lg)))
-    rids, rtw, _ = oracle.topk(r["logits"], k)
-    assert np.array_equal(r["ids"], rids) and _same_f32(r["tw"], rtw)
-    # gate/up on the GPU's routing
-    act, det = oracle.gate_up(inp["x"], r["ids"], k, inp, I, want_detail=True)
-    G.check_act(r["act"], act, det, label)
-    # down on the GPU's act
-    y, ydet = oracle.down(r["act"], r["ids"], inp, H, want_detail=True)
-    G.check_y(r["y"], y, ydet, label)
-    sh = None
-    if "sgu" in inp:
-        sact, sh_ref, sdet = oracle.shared_expert(inp["x"], inp["sgu"], inp["sdown"], True)
-        G.check_act(r["sact"], sact, sdet["gate_up"], label + " shared")
-        zeros = np.zeros(cfg["M"], np.int32)
-        sh2, shdet = oracle.down(r["sact"], zeros, dict(bw2=inp["sdown"][None]), H, True)
-        G.check_y(r["sh"], sh2, shdet, label + " shared")
-        sh = r["sh"]
-    # combine: bit-exact on the GPU's y, tw and shared output
-    out_c, _ = oracle.combine(r["y"], r["tw"], sh, k)
-    assert np.array_equal(r["out"], out_c), "combine differs"
-    # end to end against the oracle's own routing
-    full = oracle.moe_block(inp)
-    same = np.all(full["ids"] == r["ids"], axis=1)
-    ulps = G.end_to_end_ulps(r["out"], full, k, rows=same)
-    _say(f"{label}: tokens {cfg['M']}, near-tie flips {int((~same).sum())}, "
-         f"max ulp(m) {ulps.max() if ulps.size else 0:.3f}, "
-         f"mean nonzero {np.mean(ulps > 0) if ulps.size else 0:.4f}")
-    assert ulps.size == 0 or ulps.max() <= 2.0
-    return full
-
-
 @pytest.mark.parametrize("M,E,k,H,I,SI", [
     (1, 8, 2, 256, 128, 128),
     (5, 16, 4, 256, 128, 128),
@@ -183,7 +144,7 @@ def test_decode_small_stagewise(M, E, k, H, I, SI):
     _say(f"decode small M={M} E={E} k={k} H={H} I={I} SI={SI}")
     inp = synth.make_small(200 + M + E, M=M, H=H, E=E, I=I, SI=SI, top_k=k, router_std=0.3)
     r = G.run_block(fm, inp, "decode")
-    _stagewise(inp, r, "decode")
+    G.stagewise(inp, r)
 
 
 @pytest.mark.parametrize("M,E,k,H,I,SI", [(4, 8, 2, 256, 128, 128), (9, 16, 4, 512, 256, 256)])
@@ -192,7 +153,7 @@ def test_bf16_decode_small_stagewise(M, E, k, H, I, SI):
     inp = synth.make_small(300 + M, M=M, H=H, E=E, I=I, SI=SI, top_k=k, experts="bf16",
                            router_std=0.3)
     r = G.run_block(fm, inp, "bf16_decode")
-    _stagewise(inp, r, "bf16_decode")
+    G.stagewise(inp, r)
 
 
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3])
@@ -202,7 +163,7 @@ def test_decode_full_size_configs(cfg):
     inp = synth.make_inputs(cfg)
     path = "bf16_decode" if c["experts"] == "bf16" else "decode"
     r = G.run_block(fm, inp, path)
-    _stagewise(inp, r, path)
+    G.stagewise(inp, r)
 
 
 def test_forced_routing_and_determinism():
@@ -234,4 +195,4 @@ def test_decode_edge_cases():
     for (E, k) in ((8, 8), (1, 1)):
         inp = synth.make_small(510 + E, M=7, H=256, E=E, I=128, SI=128, top_k=k, router_std=0.3)
         r = G.run_block(fm, inp, "decode")
-        _stagewise(inp, r, "decode")
+        G.stagewise(inp, r)
