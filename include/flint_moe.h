@@ -29,8 +29,14 @@
  *    non-zero status means nothing was queued (FLINT_ERR_HIP: a HIP launch
  *    failed; flint_last_hip_error() gives its hipError_t).
  *  - Device pointers must be 16-byte aligned (FLINT_ERR_ALIGN otherwise).
- *  - Shapes: 1 <= top_k <= E <= 256; H % 256 == 0, 256 <= H <= 8192;
- *    I % 128 == 0, 128 <= I <= 4096; SI (shared width) 0 or I-like.
+ *  - Shapes (FLINT_ERR_SHAPE otherwise): 1 <= top_k <= E <= 256, and
+ *      decode entry points: M <= 64, M * top_k <= 512, (H, I) one of
+ *        (2048, 768), (256, 128), (256, 256), (512, 128), (512, 256),
+ *        shared width SI == I (or no shared expert);
+ *      flint_moe_grouped: any M with M * top_k <= 2^30; H % 128 == 0,
+ *        128 <= H <= 8192; I % 64 == 0, 64 <= I <= 8192; SI % 64 == 0,
+ *        SI <= 8192 (0 = no shared expert);
+ *      flint_moe_route: H in {256, 512, 1024, 2048, 4096}, M <= 16376.
  *  - A workspace is used by one stream at a time: its counters are reset by
  *    the kernels themselves, so launches using one workspace must be
  *    serialised on one stream (as the pages require of their route counter).
@@ -142,7 +148,7 @@ int flint_moe_topk(const uint16_t *logits, int M, int E, int top_k, int32_t *ids
 
 /* Router (page "vllm.models.flint.ops.moe", route / _router_kernel): bf16
  * logits of x [M, H] against router [E, H], then top-k as flint_moe_topk.
- * logits (may be NULL) [M, E].  Any M >= 1. */
+ * logits (may be NULL) [M, E].  0 <= M <= 16376 (M = 0 queues nothing). */
 int flint_moe_route(const uint16_t *x, const uint16_t *router, int M, int H, int E,
                     int top_k, uint16_t *logits, int32_t *ids, float *tw,
                     void *ws, size_t ws_bytes, void *stream);

@@ -195,7 +195,6 @@ int flint_moe_topk(const uint16_t *logits, int M, int E, int top_k, int32_t *ids
   if (!logits || !ids || !tw) return FLINT_ERR_NULL;
   if (!aligned16(logits) || !aligned16(ids) || !aligned16(tw) || (scores && !aligned16(scores)))
     return FLINT_ERR_ALIGN;
-  if (M == 0) return FLINT_OK;
   return hip_status(launch_topk(logits, M, E, top_k, ids, tw, scores, (hipStream_t)stream));
 }
 
