@@ -42,6 +42,7 @@ Workspace carve_workspace(void *base, int M, int H, int E, int I, int SI, int to
   w.sync = static_cast<DecodeSync *>(take(sizeof(DecodeSync)));
   w.route_counters = static_cast<int32_t *>(take(sizeof(int32_t) * kRouteCounterWords));
   w.logits = static_cast<uint16_t *>(take(2 * (size_t)M * E));
+  w.tlog = static_cast<unsigned long long *>(take(8 * (size_t)M * E));
   w.ids = static_cast<int32_t *>(take(4 * P));
   w.tw = static_cast<float *>(take(4 * P));
   w.plan.n_active = static_cast<int32_t *>(take(16));
@@ -124,6 +125,7 @@ int run_decode(int fmt, const uint16_t *x, const uint16_t *router, const void *w
   a.ids_in = forced ? dbg->ids_in : nullptr;
   a.tw_in = forced ? dbg->tw_in : nullptr;
   a.logits = logits;
+  a.tlog = W.tlog;
   a.ids = forced && !(dbg->ids_out) ? const_cast<int32_t *>(dbg->ids_in) : ids;
   a.tw = forced && !(dbg->tw_out) ? const_cast<float *>(dbg->tw_in) : tw;
   a.act = act;

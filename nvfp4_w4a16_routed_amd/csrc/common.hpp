@@ -11,6 +11,7 @@ constexpr int kWave = 64;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t v2u32_t;
 
 // ----------------------------------------------------------------- bf16
 
@@ -179,6 +180,24 @@ __device__ __forceinline__ bool wait_at_least(const int *p, int target) {
 }
 
 // ------------------------------------------------------------ memory ops
+
+// Buffer descriptor of `bytes` bytes at p (raw, untyped; word 3 as the
+// gfx9-family raw buffer accesses expect).  At most 2^31 - 1 bytes.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, size_t bytes) {
+  const int n = bytes > 0x7fffffffu ? 0x7fffffff : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, n, 0x00020000);
+}
+
+// A byte offset past the end of every descriptor above (they hold fewer than
+// 2^31 bytes), also after adding a few KB: buffer loads from it return zero
+// without touching memory and buffer stores to it are dropped.  Used to keep
+// the number of memory instructions on a path fixed.
+constexpr uint32_t kOOB = 0x80000000u;
+
+// Cache-policy operands of buffer accesses: streaming (non-temporal) reads,
+// and stores performed at device scope (the SC1 bit).
+constexpr int kPolicyStream = 2;
+constexpr int kPolicyDevice = 16;
 
 __device__ __forceinline__ u32x4_t load16(const void *p) {
   return *reinterpret_cast<const u32x4_t *>(p);

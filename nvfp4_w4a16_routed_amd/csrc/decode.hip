@@ -11,33 +11,38 @@
 // The shared expert follows the same rule with bf16 weights and no alpha.
 //
 // Instead of the pages' three programmatically chained launches, one
-// persistent launch (as many blocks as the GPU holds at once) runs every
-// step.  The weight bytes of the touched experts are streamed exactly once,
-// each wave owning a contiguous run of equal-sized work items and loading
-// the next item while it computes the current one.
+// persistent launch (one 16-wave block per compute unit) runs every step.
+// The weight bytes of the touched experts are streamed exactly once.
 //
-//   phase A  block-level items, no dependencies except as noted:
-//            [routing: (8 tokens, 8 experts) per block]
-//            [shared gate/up: 8 row pairs per block]
-//            A routing block tells every block that its logits are written.
-//   top-k    every block reads the logits and computes the top-k of every
-//            token and the routing plan (touched experts in ascending order
-//            and their pairs) in its own LDS: no plan is exchanged.
-//   phase B  routed gate/up items (touched expert, row pairs), slot-major.
-//   phase C  the first blocks: shared down (32 rows per block, after every
-//            shared gate/up block); the other blocks' waves: routed down
-//            items (touched expert, output rows), slot-major; a wave loads
-//            its first items' weights, then waits only for the gate/up waves
-//            of its own experts.
-//   combine  32 output rows per item, after the down waves covering them.
+//   phase A  started at once, while routing is in progress:
+//            [routing blocks: logits of (8 tokens, 16 experts) per block,
+//             each written with the call's sequence number, then a flag]
+//            [shared gate/up: one row pair per wave, spread over all blocks]
+//            [shared down: a few rows per wave, spread over all blocks,
+//             after every shared gate/up]
+//   top-k    in every block, waves without shared work wait for the routing
+//            flags, read the logits and compute the top-k of every token;
+//            the wave that finishes the last token builds the routing plan
+//            (touched experts in ascending order and their pairs) in the
+//            block's LDS: no plan is exchanged and no block barrier is used.
+//   phase B  routed gate/up items (touched expert, row pairs): each block
+//            owns a contiguous share of equal cost, and its waves take the
+//            share's items one at a time from a counter in LDS (waves of a
+//            compute unit run at different speeds; taking work as they go
+//            evens that out).  The last wave of the block to finish raises
+//            the block's flag.
+//   phase C  routed down items (touched expert, output rows), shared out the
+//            same way; an item first waits for the flags of the blocks that
+//            own its expert's gate/up items.
+//   combine  32 output rows per item, after the down items covering them.
 //
-// Completion is signalled with flags that hold the call's sequence number
-// (unique per call), written after the flagged data is performed at device
-// scope, so nothing has to be reset and no atomic read-modify-write is
-// used (on one address they serialise at the memory side).  A wave
-// waits only for work of an earlier phase, and every block of the grid is
-// resident, so every wait ends; each wait also gives up after a bounded
-// number of polls so a misused workspace cannot hang the GPU.
+// Completion is signalled with values that carry the call's sequence
+// number (unique per call), written after the data they cover is performed
+// at device scope, so nothing has to be reset and no atomic read-modify-
+// write touches global memory (on one address they serialise at the memory
+// side).  A wave waits only for work of an earlier phase, and every block of
+// the grid is resident, so every wait ends; each wait also gives up after a
+// bounded number of polls so a misused workspace cannot hang the GPU.
 #include "common.hpp"
 #include "internal.hpp"
 #include "rowdot.hpp"
@@ -46,14 +51,16 @@ namespace flint {
 
 namespace {
 
-constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / kWave;  // 8
-constexpr int kRouteTokens8 = 8;          // tokens per routing block
-constexpr int kXLdsBytes = 32768;         // x staged in LDS when M * H * 2 fits
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / kWave;  // 16
+constexpr int kRouteTokens = 4;           // tokens per routing item (one load round trip)
+constexpr int kXLdsBytes = 65536;         // x staged in LDS when M * H * 2 fits
+constexpr int kSliceBytes = 4096;         // per-wave LDS slice (act cache, combine)
+constexpr int kCacheLdsBytes = kWaves * kSliceBytes;
 // Cache-policy operand of a direct global->LDS load that reads at device
 // scope (the SC1 bit, as the device-scope loads in common.hpp use).
 constexpr int kCachePolicyDevice = 16;
-// Register budget: at least this many waves per SIMD (two 8-wave blocks per
+// Register budget: at least this many waves per SIMD (one 16-wave block per
 // CU), so enough weight bytes are in flight per CU.
 constexpr int kWavesPerEU = 4;
 
@@ -71,6 +78,7 @@ struct Params {
   const int32_t *ids_in; // forced routing (NULL = route)
   const float *tw_in;
   uint16_t *logits;
+  unsigned long long *tlog;  // [M, E] (seq << 32) | bf16 bits of the logit
   int32_t *ids;
   float *tw;
   uint16_t *act;
@@ -82,22 +90,39 @@ struct Params {
   int seq;
   int M, E, top_k;
   int nb;             // blocks in the grid
-  int n_route;        // routing blocks (0 with forced routing)
-  int n_sgu, n_sdn;   // shared gate/up and shared down blocks (0 = none)
+  int n_route;        // routing items (0 with forced routing)
+  int n_sgu, n_sdn;   // shared gate/up items (row pairs) and shared down items (0 = none)
 #ifdef FLINT_TRACE
   long long *trace;   // [waves][16] s_memrealtime stamps (timing builds only)
 #endif
 };
 
 #ifdef FLINT_TRACE
-#define TRACE(P, slot)                                                                       \
-  do {                                                                                       \
-    if (lane_id() == 0)                                                                      \
-      (P).trace[((size_t)blockIdx.x * kWaves + wave_id()) * 16 + (slot)] =                   \
-          __builtin_amdgcn_s_memrealtime();                                                  \
+// Timing builds: each wave stamps s_memrealtime into LDS (no global store
+// that a later wait would include) and writes its stamps out at the end.
+__shared__ long long g_trace_lds[kWaves * 16];
+#define TRACE(P, slot)                                                        \
+  do {                                                                        \
+    if (lane_id() == 0) g_trace_lds[wave_id() * 16 + (slot)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#define TRACE_INIT()                                                          \
+  do {                                                                        \
+    if (lane_id() < 16) g_trace_lds[wave_id() * 16 + lane_id()] = 0;          \
+  } while (0)
+#define TRACE_FLUSH(P)                                                        \
+  do {                                                                        \
+    if (lane_id() < 16)                                                       \
+      (P).trace[((size_t)blockIdx.x * kWaves + wave_id()) * 16 + lane_id()] = \
+          g_trace_lds[wave_id() * 16 + lane_id()];                            \
   } while (0)
 #else
 #define TRACE(P, slot) \
+  do {                 \
+  } while (0)
+#define TRACE_INIT() \
+  do {               \
+  } while (0)
+#define TRACE_FLUSH(P) \
   do {                 \
   } while (0)
 #endif
@@ -111,12 +136,15 @@ struct Geo {
   using SDN = DownGeo<kBf16, I>;    // shared down
   static constexpr int N_GU = I / GU::RP;  // wave items per expert
   static constexpr int N_DN = H / DN::RW;
-  static constexpr int SGU_BLOCK = kWaves * SGU::RP;  // shared row pairs per block
-  static constexpr int SDN_BLOCK = kWaves * SDN::RW;  // shared rows per block
-  static constexpr int CB = SDN_BLOCK > DN::RW ? SDN_BLOCK : DN::RW;  // combine rows
-  static_assert(I % GU::RP == 0 && I % SGU_BLOCK == 0, "gate/up items");
-  static_assert(H % DN::RW == 0 && H % SDN_BLOCK == 0 && H % CB == 0, "down items");
-  static_assert(CB % DN::RW == 0 && CB == SDN_BLOCK, "combine rows");
+  static constexpr int CB = DN::RW > 32 ? DN::RW : 32;  // combine rows per item
+  // results per vector of an item, the most of the four item kinds
+  static constexpr int NV_MAX = GU::RP > DN::RW ? (GU::RP > SDN::RW ? GU::RP : SDN::RW)
+                                                : (DN::RW > SDN::RW ? DN::RW : SDN::RW);
+  static constexpr int OUT_BYTES = kWave * (NV_MAX > SGU::RP ? NV_MAX : SGU::RP) * 2;
+  static_assert(OUT_BYTES <= kSliceBytes / 2, "output buffer");
+  static_assert(I % GU::RP == 0 && I % SGU::RP == 0, "gate/up items");
+  static_assert(H % DN::RW == 0 && H % SDN::RW == 0 && H % CB == 0, "down items");
+  static_assert(CB % DN::RW == 0 && CB % SDN::RW == 0, "combine rows");
 };
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
@@ -166,6 +194,13 @@ struct Route {
   int cum_gu[kMaxExperts + 1];  // cost before slot s of the gate/up items
   int cum_dn[kMaxExperts + 1];  // same for the down items
   int n_active;
+  int next_b, next_c;  // next item of the block's phase B / C share (relative)
+  int done_b, done_c;  // waves of the block done with phase B / C
+  int done_sg, done_sd;  // waves of the block done with shared gate/up / down
+  int topk_done;         // tokens whose top-k is in ids / tw
+  int plan_ready;        // the plan is built
+  int x_staged;          // waves whose part of x is in LDS
+  int sg_ready;          // every shared gate/up block is done
 };
 
 // Work balance.  Item (s, j) of a phase (slot s, j < N items per slot)
@@ -197,16 +232,130 @@ __device__ __forceinline__ int owner(const Route &R, const int *cum, int s, int 
   return (cum[s] + j * item_cost(R, s)) / Q;
 }
 
-// Top-k of token t by one wave (top_k <= E <= 256) into LDS.
-__device__ void topk_token(const Params &P, int t, Route &R) {
+// Top-k of token t by one wave (top_k <= E <= 256) into LDS.  The logits
+// are polled until every one carries this call's sequence number (bounded:
+// after ~2^20 polls it goes on with what it read, so the kernel still
+// ends).  Block 0 also writes the plain bf16 logits.  The token's selected
+// experts are also OR-ed into R.tokmask.
+//
+// Selection: the keys (the logit's order-preserving image, then the
+// reversed expert index) are unique, so the top_k largest are exactly those
+// >= the top_k-th largest key, found bit by bit from the top with ballot
+// counts.  The selected keys are then ranked among themselves (descending
+// key = the pages' selection order), which fixes the order of ids, of the
+// weights and of the fp32 sum of the scores.
+__device__ void topk_token(const Params &P, int t, Route &R, int *scratch) {
   const int lane = lane_id();
   const int E = P.E, k = P.top_k;
-  const uint16_t *lrow = P.logits + (size_t)t * E;
+  const unsigned long long *trow = P.tlog + (size_t)t * E;
+  // four slots per lane, expert lane + 64 i; slots past E read expert E - 1
+  // and are masked, so every load is issued at once and nothing branches
+  int ee[4];
+  bool valid[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ee[i] = lane + kWave * i;
+    valid[i] = ee[i] < E;
+    ee[i] = valid[i] ? ee[i] : E - 1;
+  }
+  unsigned long long v[4];
+  for (int it = 0, nap = 1; it < (1 << 20); ++it) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = ld_dev(&trow[ee[i]]);
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ok &= !valid[i] || (uint32_t)(v[i] >> 32) == (uint32_t)P.seq;
+    if (__all(ok)) break;
+    for (int z = 0; z < nap; ++z) __builtin_amdgcn_s_sleep(2);
+    nap = nap < 8 ? nap * 2 : 8;
+  }
+  TRACE(P, 13);
+  int keys[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t bits = (uint32_t)v[i] & 0xffffu;
+    keys[i] = valid[i] ? topk_key(bits, ee[i], E) : -1;
+  }
+  if (blockIdx.x == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (valid[i]) P.logits[(size_t)t * E + ee[i]] = (uint16_t)(v[i] & 0xffffu);
+  }
+  // the top_k-th largest key: keys are 24-bit, non-negative when valid
+  int thr = 0;
+#pragma unroll
+  for (int bit = 23; bit >= 0; --bit) {
+    const int cand = thr | (1 << bit);
+    const int cnt = __popcll(__ballot(keys[0] >= cand)) + __popcll(__ballot(keys[1] >= cand)) +
+                    __popcll(__ballot(keys[2] >= cand)) + __popcll(__ballot(keys[3] >= cand));
+    thr = cnt >= k ? cand : thr;
+  }
+  // compact the selected keys into scratch[0 .. k)
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool sel = keys[i] >= thr;
+    const unsigned long long m = __ballot(sel);
+    if (sel) scratch[base + __popcll(m & ((1ull << lane) - 1ull))] = keys[i];
+    base += __popcll(m);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // lanes j < top_k (top_k <= 64 here): a selected key, its rank among the
+  // selected (0 = largest = first in the pages' order) and its score
+  const int key = lane < k ? scratch[lane] : -1;
+  int rank = 0;
+  for (int j = 0; j < k; ++j) rank += __builtin_amdgcn_readlane(key, j) > key;
+  float sc = 0.0f;
+  if (lane < k) {
+    const float l = bf16_to_f32(key_bits(key));
+    const float a = (float)exp(-(double)l);  // correctly rounded for every bf16 l
+    const float d = 1.0f + a;
+    sc = 1.0f / d;
+  }
+  // the fp32 sum of the scores in selection order, one addition at a time
+  float S = 0.0f;
+  for (int r = 0; r < k; ++r) {
+    const int src = __builtin_ctzll(__ballot(rank == r && lane < k));
+    S = S + __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc), src));
+  }
+  const float D = S + 1e-20f;
+  if (lane < k) {
+    const int e = E - 1 - (key & 0xff);
+    R.ids[t * k + rank] = e;
+    R.tw[t * k + rank] = round_bf16(sc / D);
+    atomicOr(&R.tokmask[e], 1ull << t);
+  }
+}
+
+// The same selection for top_k > 64 (k rounds of "take the largest key").
+__device__ void topk_token_long(const Params &P, int t, Route &R) {
+  const int lane = lane_id();
+  const int E = P.E, k = P.top_k;
+  const unsigned long long *trow = P.tlog + (size_t)t * E;
+  unsigned long long v[4] = {0ull, 0ull, 0ull, 0ull};
+  for (int it = 0, nap = 1; it < (1 << 20); ++it) {
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + kWave * i;
+      if (e < E) {
+        v[i] = ld_dev(&trow[e]);
+        ok &= (uint32_t)(v[i] >> 32) == (uint32_t)P.seq;
+      }
+    }
+    if (__all(ok)) break;
+    for (int z = 0; z < nap; ++z) __builtin_amdgcn_s_sleep(2);
+    nap = nap < 8 ? nap * 2 : 8;
+  }
   int keys[4], sel[4] = {-1, -1, -1, -1};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    int e = lane + kWave * i;
-    keys[i] = (e < E) ? topk_key(ld_dev(&lrow[e]), e, E) : -1;
+    const int e = lane + kWave * i;
+    const uint32_t bits = (uint32_t)v[i] & 0xffffu;
+    keys[i] = (e < E) ? topk_key(bits, e, E) : -1;
+    if (blockIdx.x == 0 && e < E) P.logits[(size_t)t * E + e] = (uint16_t)bits;
   }
   for (int j = 0; j < k; ++j) {
     int best = wave_max_i32(max(max(keys[0], keys[1]), max(keys[2], keys[3])));
@@ -221,91 +370,91 @@ __device__ void topk_token(const Params &P, int t, Route &R) {
   for (int i = 0; i < 4; ++i) {
     s[i] = 0.0f;
     if (kWave * i + lane < k) {
-      float l = bf16_to_f32(key_bits(sel[i]));
-      float a = (float)exp(-(double)l);  // correctly rounded for every bf16 l
-      float d = 1.0f + a;
+      const float l = bf16_to_f32(key_bits(sel[i]));
+      const float a = (float)exp(-(double)l);
+      const float d = 1.0f + a;
       s[i] = 1.0f / d;
     }
   }
-  float S = 0.0f;  // in selection order, one addition at a time
+  float S = 0.0f;
   for (int j = 0; j < k; ++j) {
     const int i = j >> 6;
-    const float v = (i == 0) ? s[0] : (i == 1) ? s[1] : (i == 2) ? s[2] : s[3];
-    S = S + __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), j & (kWave - 1)));
+    const float v2 = (i == 0) ? s[0] : (i == 1) ? s[1] : (i == 2) ? s[2] : s[3];
+    S = S + __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v2), j & (kWave - 1)));
   }
   const float D = S + 1e-20f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int j = kWave * i + lane;
     if (j < k) {
-      R.ids[t * k + j] = E - 1 - (sel[i] & 0xff);
+      const int e = E - 1 - (sel[i] & 0xff);
+      R.ids[t * k + j] = e;
       R.tw[t * k + j] = round_bf16(s[i] / D);
+      atomicOr(&R.tokmask[e], 1ull << t);
     }
   }
 }
 
-// Exclusive prefix sum over the wave (lane order).
+// Exclusive prefix sum over the wave (lane order), with DPP: shifts by 1,
+// 2, 4, 8 inside each 16-lane row, then the running totals of rows 0 and 0-1
+// carried into the later rows.
 __device__ __forceinline__ int wave_exclusive_scan(int v) {
   int x = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int t = __shfl_up(x, o, kWave);
-    if (lane_id() >= o) x += t;
-  }
+  x += dpp_i32<0x111>(x);  // row_shr:1 (lanes shifted in from outside the row read 0)
+  x += dpp_i32<0x112>(x);  // row_shr:2
+  x += dpp_i32<0x114>(x);  // row_shr:4
+  x += dpp_i32<0x118>(x);  // row_shr:8
+  x += dpp_i32<kDppBcast15, 0xA>(x, 0);  // rows 1, 3 += last lane of rows 0, 2
+  x += dpp_i32<kDppBcast31, 0xC>(x, 0);  // rows 2, 3 += lane 31
   return x - v;
 }
 
-// Routing plan from R.ids: touched experts ascending (slot order), pairs of
-// each expert ascending (an expert has at most one pair per token), and the
-// cumulative item costs of phases B and C (GU_ITEMS, DN_ITEMS items per
-// slot).  Ends with the block synchronised.
+// Routing plan from R.ids and R.tokmask, built by one wave: touched experts ascending
+// (slot order), pairs of each expert ascending (an expert has at most one
+// pair per token), and the cumulative item costs of phases B and C
+// (GU_ITEMS, DN_ITEMS items per slot).  Ends by raising R.plan_ready.
 template <int GU_ITEMS, int DN_ITEMS>
-__device__ void build_plan(const Params &P, Route &R) {
-  const int npairs = P.M * P.top_k, k = P.top_k;
-  for (int e = threadIdx.x; e < kMaxExperts; e += kThreads) R.tokmask[e] = 0ull;
-  __syncthreads();
-  for (int p = threadIdx.x; p < npairs; p += kThreads) {
-    const int e = R.ids[p];
-    if ((unsigned)e < (unsigned)P.E) atomicOr(&R.tokmask[e], 1ull << (p / k));  // bad ids dropped
+__device__ void build_plan_wave(const Params &P, Route &R) {
+  const int npairs = P.M * P.top_k, k = P.top_k, lane = lane_id();
+  // R.tokmask (tokens that selected each expert) was filled with the ids
+  // lane l holds experts 4l .. 4l + 3
+  int cnt[4], flg[4], c = 0, f = 0, u = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * lane + i;
+    cnt[i] = e < P.E ? __popcll(R.tokmask[e]) : 0;
+    flg[i] = cnt[i] > 0;
+    c += cnt[i];
+    f += flg[i];
+    u += flg[i] ? 2 + cnt[i] : 0;
   }
-  __syncthreads();
-  if (wave_id() == 0) {
-    // lane l holds experts 4l .. 4l + 3
-    int cnt[4], flg[4], c = 0, f = 0, u = 0;
+  int base = wave_exclusive_scan(c), slot = wave_exclusive_scan(f);
+  int cost = wave_exclusive_scan(u);  // in units of one item per slot
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = 4 * lane_id() + i;
-      cnt[i] = e < P.E ? __popcll(R.tokmask[e]) : 0;
-      flg[i] = cnt[i] > 0;
-      c += cnt[i];
-      f += flg[i];
-      u += flg[i] ? 2 + cnt[i] : 0;
-    }
-    int base = wave_exclusive_scan(c), slot = wave_exclusive_scan(f);
-    int cost = wave_exclusive_scan(u);  // in units of one item per slot
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = 4 * lane_id() + i;
-      if (flg[i]) {
-        R.slot_of[e] = slot;
-        R.active[slot] = e;
-        R.offs[slot] = base;
-        R.cum_gu[slot] = cost * GU_ITEMS;
-        R.cum_dn[slot] = cost * DN_ITEMS;
-      }
-      base += cnt[i];
-      slot += flg[i];
-      cost += flg[i] ? 2 + cnt[i] : 0;
-    }
-    if (lane_id() == kWave - 1) {
-      R.n_active = slot;
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * lane + i;
+    if (flg[i]) {
+      R.slot_of[e] = slot;
+      R.active[slot] = e;
       R.offs[slot] = base;
       R.cum_gu[slot] = cost * GU_ITEMS;
       R.cum_dn[slot] = cost * DN_ITEMS;
     }
+    base += cnt[i];
+    slot += flg[i];
+    cost += flg[i] ? 2 + cnt[i] : 0;
   }
-  __syncthreads();
-  for (int p = threadIdx.x; p < npairs; p += kThreads) {
+  if (lane == kWave - 1) {
+    R.next_b = R.next_c = R.done_b = R.done_c = 0;
+    R.n_active = slot;
+    R.offs[slot] = base;
+    R.cum_gu[slot] = cost * GU_ITEMS;
+    R.cum_dn[slot] = cost * DN_ITEMS;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (int p = lane; p < npairs; p += kWave) {
     const int ee = R.ids[p];
     if ((unsigned)ee < (unsigned)P.E) {
       const int t = p / k;
@@ -313,7 +462,26 @@ __device__ void build_plan(const Params &P, Route &R) {
       R.pairs[R.offs[R.slot_of[ee]] + rank] = p;
     }
   }
-  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  if (lane == 0) __hip_atomic_store(&R.plan_ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Waits (bounded) until an LDS counter of the block reaches n.
+__device__ __forceinline__ void wait_lds_at_least(int *c, int n) {
+  for (int it = 0; it < (1 << 22); ++it) {
+    if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= n) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// Waits (LDS, bounded) until the block's plan is built.
+__device__ __forceinline__ void wait_plan(Route &R) {
+  for (int it = 0; it < (1 << 22); ++it) {
+    if (__hip_atomic_load(&R.plan_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
 // --------------------------------------------------------- phase A items
@@ -344,69 +512,71 @@ __device__ __forceinline__ void stage_rows(uint16_t *dst, const uint16_t *src, i
   copy_to_lds<DEVICE>(dst, src, nr * K / 8, wave_id(), kWaves);
 }
 
-// Routing block r: logits of experts 8 * (r % nEG) + wave for the 8 tokens
-// of group r / nEG, then a flag to every block.  x (of the group, or all of
-// it when it fits) is staged in LDS unless it already is.
+// Routing block r: logits of experts kWaves * (r % nEG) + wave for the 8
+// tokens of group r / nEG, each stored with the call's sequence number in
+// one 8-byte word, then the block's flag.  x (of the group, or all of it
+// when it fits) is staged in LDS unless it already is.
+// Routing item r (one wave): logits of expert r % E for the kRouteTokens
+// tokens of group r / E, each stored with the call's sequence number in one 8-byte
+// word (the value and its "written" mark arrive together).  x is read from
+// global memory (it is an input), so the item needs no LDS and can start at
+// once.
 template <int H>
-__device__ void route_block(const Params &P, int r, uint16_t *xs, bool x_all, bool &staged) {
+__device__ void route_item(const Params &P, int r) {
   constexpr int NC = H / 8;
   constexpr int CPL = (NC + kWave - 1) / kWave;
   const int lane = lane_id();
-  const int nEG = (P.E + kWaves - 1) / kWaves;
-  const int t0 = (r / nEG) * kRouteTokens8;
-  const int nt = min(kRouteTokens8, P.M - t0);
-  const int e = (r % nEG) * kWaves + wave_id();
-  // router row first: its loads overlap the staging of x
+  const int e = r % P.E;
+  const int t0 = (r / P.E) * kRouteTokens;
+  const int nt = min(kRouteTokens, P.M - t0);
   u32x4_t w[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
     const int c = lane + kWave * i;
-    w[i] = (e < P.E && c < NC) ? load16(P.router + (size_t)e * H + c * 8) : u32x4_t{0, 0, 0, 0};
+    w[i] = c < NC ? load16(P.router + (size_t)e * H + c * 8) : u32x4_t{0, 0, 0, 0};
   }
-  const int r0 = x_all ? 0 : t0;
-  if (!(x_all && staged)) {
-    __syncthreads();  // earlier readers of the staging area are done
-    stage_rows<H, false>(xs, P.x + (size_t)r0 * H, x_all ? P.M : nt);
-    staged = x_all;
-  }
-  __syncthreads();
-  const uint16_t *xg = xs + (size_t)(t0 - r0) * H;
-  if (e < P.E) {
-    for (int ti = 0; ti < nt; ++ti) {
-      float acc = 0.0f;
+  const unsigned long long tag = (unsigned long long)(uint32_t)P.seq << 32;
+  for (int g = 0; g < nt; g += 4) {
+    u32x4_t xv[4][CPL];
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
         const int c = lane + kWave * i;
-        if (c < NC) {
-          const u32x4_t v = load16(xg + (size_t)ti * H + c * 8);
-          acc = dot2_bf16(w[i][0], v[0], acc);
-          acc = dot2_bf16(w[i][1], v[1], acc);
-          acc = dot2_bf16(w[i][2], v[2], acc);
-          acc = dot2_bf16(w[i][3], v[3], acc);
-        }
+        xv[ti][i] = (g + ti < nt && c < NC) ? load16(P.x + (size_t)(t0 + g + ti) * H + c * 8)
+                                            : u32x4_t{0, 0, 0, 0};
+      }
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        acc = dot2_bf16(w[i][0], xv[ti][i][0], acc);
+        acc = dot2_bf16(w[i][1], xv[ti][i][1], acc);
+        acc = dot2_bf16(w[i][2], xv[ti][i][2], acc);
+        acc = dot2_bf16(w[i][3], xv[ti][i][3], acc);
       }
       acc = group_sum<kWave>(acc);
-      if (lane == kWave - 1) st_dev(&P.logits[(size_t)(t0 + ti) * P.E + e], (uint16_t)f32_to_bf16(acc));
+      if (lane == kWave - 1 && g + ti < nt)
+        st_dev(&P.tlog[(size_t)(t0 + g + ti) * P.E + e], tag | f32_to_bf16(acc));
     }
   }
-  stores_performed();
-  __syncthreads();
-  for (int b = threadIdx.x; b < P.nb; b += kThreads) st_dev(&P.sync->go[b][r], P.seq);
 }
 
-// Gate/up of one wave on given weights: vector i (i < np) is x[tok(i)], its
-// result goes to dst[pair(i) * I + n].  x is read from xl (LDS) when
-// non-NULL, else from global memory.
-template <int FMT, int H, int I, typename Tok, typename Pair>
+// Gate/up of one wave on given weights for vectors i < np (np <= 64):
+// vector i is x[tok(i)], read from xl (LDS) when non-NULL, else from global
+// memory.  Results go to the wave's output buffer: ob[i * RP + row] (bf16)
+// for the item's RP row pairs.
+template <int FMT, int H, int I, typename Tok>
 __device__ __forceinline__ void gate_up_compute(const Params &P, const GateUpW<FMT, H, I> &W,
-                                                float alpha, int n_base, int np, Tok tok,
-                                                Pair pair, const uint16_t *xl, uint16_t *dst) {
+                                                float alpha, int np, Tok tok, const uint16_t *xl,
+                                                uint16_t *ob) {
   using Map = RowMap<FMT, H>;
   using G = GateUpGeo<FMT, H>;
   const int lane = lane_id();
   const int r = lane / Map::LPR, q = lane % Map::LPR;
   for (int i = 0; i < np; ++i) {
-    const int t = tok(i), p = pair(i);
+    const int t = tok(i);
     float acc[2 * G::NSL];
     if (xl)
       rows_dot<FMT, H, kSrcLds>(W.rows, xl + (size_t)t * H, q, acc);
@@ -421,17 +591,17 @@ __device__ __forceinline__ void gate_up_compute(const Params &P, const GateUpW<F
           gs = gs * alpha;
           us = us * alpha;
         }
-        st_dev(&dst[(size_t)p * I + n_base + s * Map::RS + r], (uint16_t)f32_to_bf16(swiglu(gs, us)));
+        ob[i * G::RP + s * Map::RS + r] = (uint16_t)f32_to_bf16(swiglu(gs, us));
       }
     }
   }
 }
 
-// Down of one wave on given weights for one vector (SRC: kSrcLds or
-// kSrcDevice); the result row goes to dst_row.
+// Down of one wave on given weights for vector j (SRC: kSrcLds or
+// kSrcDevice); its RW results go to ob[j * RW + row].
 template <int FMT, int H, int I, int SRC>
 __device__ __forceinline__ void down_one(const DownW<FMT, I> &W, const uint16_t *vec, float alpha,
-                                         int h_base, uint16_t *dst_row) {
+                                         int j, uint16_t *ob) {
   using Map = RowMap<FMT, I>;
   using G = DownGeo<FMT, I>;
   const int lane = lane_id();
@@ -443,27 +613,82 @@ __device__ __forceinline__ void down_one(const DownW<FMT, I> &W, const uint16_t 
     float val = group_sum<Map::LPR>(acc[s]);
     if (q == Map::LPR - 1) {
       if constexpr (FMT == kNvfp4) val = val * alpha;
-      st_dev(&dst_row[h_base + s * Map::RS + r], (uint16_t)f32_to_bf16(val));
+      ob[j * G::RW + s * Map::RS + r] = (uint16_t)f32_to_bf16(val);
     }
+  }
+}
+
+// Writes an item's results with one store instruction per 16 bytes: lane j
+// stores the NV bf16 values ob[j * NV ...] at byte offset off of descriptor
+// dst (kOOB for lanes without a vector: dropped), performed at device scope.
+// The stores of an item are always issued, so their number never varies.
+template <int NV>
+__device__ __forceinline__ void store_results(__amdgpu_buffer_rsrc_t dst, uint32_t off,
+                                              const uint16_t *ob) {
+  static_assert(NV == 1 || NV == 2 || NV == 4 || NV % 8 == 0, "results per vector");
+  // the item's results were written by other lanes of this wave
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint16_t *src = ob + lane_id() * NV;
+  if constexpr (NV == 1) {
+    __builtin_amdgcn_raw_buffer_store_b16(src[0], dst, off, 0, kPolicyDevice);
+  } else if constexpr (NV == 2) {
+    __builtin_amdgcn_raw_buffer_store_b32(*reinterpret_cast<const uint32_t *>(src), dst, off, 0,
+                                          kPolicyDevice);
+  } else if constexpr (NV == 4) {
+    const uint2 v = *reinterpret_cast<const uint2 *>(src);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32_t, v), dst, off, 0,
+                                          kPolicyDevice);
+  } else {
+#pragma unroll
+    for (int c = 0; c < NV / 8; ++c)
+      __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4_t *>(src + 8 * c), dst,
+                                             off + 16 * c, 0, kPolicyDevice);
   }
 }
 
 // ------------------------------------------------------------ the kernel
 
-// Routed gate/up wave items of the call: U slots x N_GU items; wave gw
-// owns [gw * C, (gw + 1) * C).
 __device__ __forceinline__ int per_wave(int items, int nw) { return (items + nw - 1) / nw; }
+
+// Next item of the block's share of a phase: one LDS counter per phase,
+// taken by lane 0 and broadcast (items come out in increasing order).
+__device__ __forceinline__ int take_item(int *ctr, int base) {
+  int v = 0;
+  if (lane_id() == 0) v = atomicAdd(ctr, 1);
+  return base + __builtin_amdgcn_readfirstlane(v);
+}
+
+// A wave is done with its phase: once the stores of all kWaves waves are
+// performed, the last of them raises the block's flag.
+__device__ __forceinline__ void block_done(int *ctr, int *flag, int seq) {
+  stores_performed();
+  if (lane_id() == 0) {
+    if (atomicAdd(ctr, 1) == kWaves - 1) st_dev(flag, seq);
+  }
+}
+
+// Block that owns item (s, j) of a phase partitioned in shares of cost Q.
+__device__ __forceinline__ int owner_block(const Route &R, const int *cum, int s, int j, int Q,
+                                           int nb) {
+  const int b = owner(R, cum, s, j, Q);
+  return b < nb ? b : nb - 1;
+}
 
 template <int FMT, int H, int I>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
 decode_kernel(Params P) {
   using Gm = Geo<FMT, H, I>;
-  using GuMap = RowMap<FMT, H>;
   using DnMap = RowMap<FMT, I>;
   constexpr int GU_RSZ = FMT == kNvfp4 ? H / 2 : H * 2;  // routed row bytes (w13)
   constexpr int DN_RSZ = FMT == kNvfp4 ? I / 2 : I * 2;  // routed row bytes (w2)
   __shared__ Route R;
-  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];  // x staging
+  // Dynamic LDS: x staging (kXLdsBytes), then one slice per wave
+  // (kSliceBytes each: the down items' activation cache, the combine's y).
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
+  uint16_t *slice = xs + kXLdsBytes / 2 + (size_t)wave_id() * (kSliceBytes / 2);
+  uint16_t *ob = slice + (kSliceBytes - Gm::OUT_BYTES) / 2;  // an item's results
 
   DecodeSync *S = P.sync;
   const int lane = lane_id(), wv = wave_id();
@@ -471,168 +696,255 @@ decode_kernel(Params P) {
   const int gw = blockIdx.x * kWaves + wv;
   const int k = P.top_k;
   const bool x_all = P.M * H * 2 <= kXLdsBytes;  // all of x fits the staging area
+  TRACE_INIT();
   TRACE(P, 0);
 
-  // ---- phase A (block items b = blockIdx.x, blockIdx.x + nb, ...)
-  const int nA = P.n_route + P.n_sgu;
-  bool staged = false;  // all of x is in the staging area
-  for (int b = blockIdx.x; b < nA; b += P.nb) {
-    if (b < P.n_route) {
-      route_block<H>(P, b, xs, x_all, staged);
-    } else if (b < P.n_route + P.n_sgu) {
-      // shared gate/up: 8 row pairs, every token (x staged in groups)
-      const int sb = b - P.n_route;
-      const int n_base = sb * Gm::SGU_BLOCK + wv * Gm::SGU::RP;
-      GateUpW<kBf16, H, I> W;
-      gate_up_load(W, P.sgu, nullptr, n_base);
-      const int G = x_all ? P.M : kRouteTokens8;
-      for (int g0 = 0; g0 < P.M; g0 += G) {
-        if (!(x_all && staged)) {
-          __syncthreads();
-          stage_rows<H, false>(xs, P.x + (size_t)g0 * H, min(G, P.M - g0));
-          staged = x_all;
-        }
-        __syncthreads();
-        gate_up_compute<kBf16, H, I>(P, W, 1.0f, n_base, min(G, P.M - g0), [](int i) { return i; },
-                                     [g0](int i) { return g0 + i; }, xs, P.sact);
-      }
-      stores_performed();
-      __syncthreads();
-      if (threadIdx.x == 0) st_dev(&S->sg[sb], P.seq);
-    }
+  if (threadIdx.x == 0) {
+    R.done_sg = R.done_sd = R.topk_done = R.plan_ready = R.x_staged = R.sg_ready = 0;
+  }
+  if (threadIdx.x < kMaxExperts) R.tokmask[threadIdx.x] = 0ull;
+  __syncthreads();  // publishes the counters
+
+  // ---- phase A1: routing items, one per wave from the last wave of each
+  // block down (item r: block r % nb); they read x from global memory.
+  for (int r = blockIdx.x + P.nb * (kWaves - 1 - wv); r < P.n_route; r += P.nb * kWaves) {
+    __builtin_amdgcn_s_setprio(3);  // on the critical path
+    route_item<H>(P, r);
+    __builtin_amdgcn_s_setprio(0);
   }
   TRACE(P, 1);
-  // Stage all of x for the gate/up items (small batches) while routing ends.
-  if (x_all && !staged) {
-    __syncthreads();
-    stage_rows<H, false>(xs, P.x, P.M);
+  // All of x in LDS when it fits (shared gate/up and phase B read it
+  // there), staged by every wave but the last; R.x_staged counts them.
+  if (x_all && wv < kWaves - 1) {
+    copy_to_lds<false>(xs, P.x, P.M * H / 8, wv, kWaves - 1);
+    if (lane == 0) atomicAdd(&R.x_staged, 1);
+  }
+  auto wait_x = [&]() {
+    if (x_all) wait_lds_at_least(&R.x_staged, kWaves - 1);
+  };
+
+  // Shared-expert items go to every block: shared gate/up items to its
+  // first nsg waves, shared down items to the next nsd waves; the remaining
+  // waves compute the top-k.
+  const int sh0 = 0;  // first block with shared items
+  const int nbs = P.nb - sh0;
+  const int bs = (int)blockIdx.x - sh0;
+  const int nsg = P.sgu ? min((P.n_sgu + nbs - 1) / nbs, kWaves / 2) : 0;
+  const int nsd = P.sgu ? min((P.n_sdn + nbs - 1) / nbs, kWaves / 2) : 0;
+
+  // ---- phase A2: shared gate/up, one row-pair item per wave (item j:
+  // block sh0 + j % nbs, wave j / nbs), every token.
+  if (P.sgu) {
+    const __amdgpu_buffer_rsrc_t rs_w = make_rsrc(P.sgu, (size_t)2 * I * H * 2);
+    const __amdgpu_buffer_rsrc_t rs_o = make_rsrc(P.sact, (size_t)P.M * I * 2);
+    for (int j = (bs >= 0 && wv < nsg) ? bs + nbs * wv : P.n_sgu; j < P.n_sgu; j += nbs * nsg) {
+      const int n_base = j * Gm::SGU::RP;
+      GateUpW<kBf16, H, I> W;
+      gate_up_load(W, rs_w, 0u, rs_w, 0u, n_base);
+      wait_x();
+      TRACE(P, 9);
+      for (int g0 = 0; g0 < P.M; g0 += kWave) {
+        const int nt = min(kWave, P.M - g0);
+        gate_up_compute<kBf16, H, I>(P, W, 1.0f, nt, [g0](int i) { return g0 + i; },
+                                     x_all ? xs : nullptr, ob);
+        store_results<Gm::SGU::RP>(
+            rs_o, lane < nt ? (uint32_t)(((g0 + lane) * I + n_base) * 2) : kOOB, ob);
+      }
+      TRACE(P, 11);
+    }
+    block_done(&R.done_sg, &S->sg[blockIdx.x], P.seq);
   }
 
-  // ---- routing of every token, in this block's LDS
-  if (P.ids_in) {
-    for (int p = threadIdx.x; p < P.M * k; p += kThreads) {
-      R.ids[p] = P.ids_in[p];
-      R.tw[p] = P.tw_in[p];
+  // ---- phase A3: shared down, one item (RW rows) per wave (item j: block
+  // sh0 + j % nbs, wave nsg + j / nbs), after every shared gate/up block.
+  // sact is staged in a part of the staging area that x does not use.
+  if (P.sgu) {
+    const __amdgpu_buffer_rsrc_t rs_w = make_rsrc(P.sdown, (size_t)H * I * 2);
+    const __amdgpu_buffer_rsrc_t rs_o = make_rsrc(P.sh, (size_t)P.M * H * 2);
+    const int free_el = kXLdsBytes / 2 - (x_all ? P.M * H : 0);
+    const int per = free_el / max(1, min(nsd, kWaves));  // bf16 per shared-down wave
+    // the wave's slice when the free part of the staging area is too small
+    constexpr int kSliceRows = (kSliceBytes - Gm::OUT_BYTES) / (2 * I);
+    static_assert(kSliceRows >= 1, "shared activations staging");
+    const int region = per >= I ? per / I * I : kSliceRows * I;
+    const int G = min(kWave, region / I);  // tokens per staged group, >= 1
+    bool waited = false;
+    const int ws = wv - nsg;  // this wave's place among the shared down waves
+    for (int j = (bs >= 0 && ws >= 0 && ws < nsd) ? bs + nbs * ws : P.n_sdn; j < P.n_sdn;
+         j += nbs * nsd) {
+      const int h_base = j * Gm::SDN::RW;
+      DownW<kBf16, I> W;
+      down_load(W, rs_w, 0u, rs_w, 0u, h_base);
+      if (!waited) {
+        // the block's first shared down wave polls the flags, the others
+        // wait for its word in LDS
+        if (ws == 0) {
+          wave_wait_flags(S->sg, sh0, sh0 + min(nbs, P.n_sgu), P.seq);
+          if (lane == 0) __hip_atomic_store(&R.sg_ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        } else {
+          wait_lds_at_least(&R.sg_ready, 1);
+        }
+        waited = true;
+      }
+      TRACE(P, 14);
+      uint16_t *sl = per >= I ? xs + (x_all ? P.M * H : 0) + (size_t)ws * region : slice;
+      for (int g0 = 0; g0 < P.M; g0 += G) {
+        const int nt = min(G, P.M - g0);
+        copy_to_lds<true>(sl, P.sact + (size_t)g0 * I, nt * I / 8, 0, 1);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (int t = 0; t < nt; ++t)
+          down_one<kBf16, H, I, kSrcLds>(W, sl + (size_t)t * I, 1.0f, t, ob);
+        store_results<Gm::SDN::RW>(
+            rs_o, lane < nt ? (uint32_t)(((g0 + lane) * H + h_base) * 2) : kOOB, ob);
+      }
+      TRACE(P, 15);
     }
-  } else {
-    if (wv == 0) wave_wait_flags(S->go[blockIdx.x], 0, P.n_route, P.seq);
-    __syncthreads();
-    TRACE(P, 2);
-    for (int t = wv; t < P.M; t += kWaves) topk_token(P, t, R);
+    block_done(&R.done_sd, &S->sd[blockIdx.x], P.seq);
   }
-  __syncthreads();
-  TRACE(P, 8);
-  build_plan<Gm::N_GU, Gm::N_DN>(P, R);
+  TRACE(P, 2);
+
+  // ---- routing of every token (waves without shared-expert items), in this
+  // block's LDS; the wave that completes the last token builds the plan.
+  {
+    // top-k waves: those with no shared-expert item (first waves: shared
+    // gate/up, last waves: shared down), token t on wave w0 + t % nfree
+    const int nfree = kWaves - nsg - nsd >= 1 ? kWaves - nsg - nsd : kWaves;
+    const int w0 = kWaves - nsg - nsd >= 1 ? nsg + nsd : 0;
+    const int slot = wv - w0;
+    __builtin_amdgcn_s_setprio(3);  // on the critical path: ahead of other waves' work
+    int mine = 0;
+    for (int t = (slot >= 0 && slot < nfree) ? slot : P.M; t < P.M; t += nfree) {
+      if (P.ids_in) {
+        for (int j = lane; j < k; j += kWave) {
+          const int e = P.ids_in[t * k + j];
+          R.ids[t * k + j] = e;
+          R.tw[t * k + j] = P.tw_in[t * k + j];
+          if ((unsigned)e < (unsigned)P.E) atomicOr(&R.tokmask[e], 1ull << t);  // bad ids dropped
+        }
+      } else if (k <= kWave) {
+        topk_token(P, t, R, reinterpret_cast<int *>(slice));
+      } else {
+        topk_token_long(P, t, R);
+      }
+      ++mine;
+    }
+    TRACE(P, 8);
+    int before = 0;
+    if (mine > 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      if (lane == 0) before = atomicAdd(&R.topk_done, mine);
+      before = __builtin_amdgcn_readfirstlane(before);
+    }
+    if (mine > 0 && before + mine == P.M) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      build_plan_wave<Gm::N_GU, Gm::N_DN>(P, R);
+    } else {
+      wait_plan(R);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  }
   if (blockIdx.x == 0)
     for (int p = threadIdx.x; p < P.M * k; p += kThreads) {
       if (P.ids != P.ids_in) P.ids[p] = R.ids[p];
       if (P.tw != P.tw_in) P.tw[p] = R.tw[p];
     }
   TRACE(P, 3);
+  wait_x();
   const int U = R.n_active;
   const uint16_t *xl = x_all ? xs : nullptr;
 
-  // ---- phase B: routed gate/up, wave gw owns items [b0, b1)
-  const int QB = max(1, per_wave(R.cum_gu[U], NW));  // cost share of a wave
+  // ---- phase B: routed gate/up; block share [b0, b1) of equal cost
+  //
+  // Memory instructions per item are fixed (every load issued, items past
+  // the share read out of range; one store per 16 result bytes), and the
+  // loop keeps them in one order -- [loads of item a] [stores of item b]
+  // [loads of item b] ... -- so the wait for an item's weights never waits
+  // for a store or for the other item's loads.
+  const int QB = max(1, per_wave(R.cum_gu[U], P.nb));
   {
-    const int b0 = first_item(R, R.cum_gu, Gm::N_GU, gw * QB);
-    const int b1 = first_item(R, R.cum_gu, Gm::N_GU, (gw + 1) * QB);
+    const int b0 = first_item(R, R.cum_gu, Gm::N_GU, blockIdx.x * QB);
+    const int b1 = first_item(R, R.cum_gu, Gm::N_GU, (blockIdx.x + 1) * QB);
+    const __amdgpu_buffer_rsrc_t rs_w = make_rsrc(P.w13, (size_t)P.E * 2 * I * GU_RSZ);
+    const __amdgpu_buffer_rsrc_t rs_s =
+        make_rsrc(FMT == kNvfp4 ? (const void *)P.s13 : (const void *)P.w13,
+                  FMT == kNvfp4 ? (size_t)P.E * 2 * I * (H / 16) : 0);
+    const __amdgpu_buffer_rsrc_t rs_o = make_rsrc(P.act, (size_t)P.M * k * I * 2);
     struct St {
       GateUpW<FMT, H, I> w;
       float alpha;
     };
     auto load = [&](St &st, int i) {
-      const int e = R.active[i / Gm::N_GU];
-      const int n_base = (i % Gm::N_GU) * Gm::GU::RP;
-      gate_up_load(st.w, P.w13 + (size_t)e * 2 * I * GU_RSZ,
-                   FMT == kNvfp4 ? P.s13 + (size_t)e * 2 * I * (H / 16) : nullptr, n_base);
+      const bool ok = i < b1;
+      const int e = __builtin_amdgcn_readfirstlane(ok ? R.active[i / Gm::N_GU] : 0);
+      const int n_base = ok ? (i % Gm::N_GU) * Gm::GU::RP : 0;
+      gate_up_load(st.w, rs_w, ok ? (uint32_t)e * 2 * I * GU_RSZ : kOOB, rs_s,
+                   ok ? (uint32_t)e * 2 * I * (H / 16) : kOOB, n_base);
       st.alpha = FMT == kNvfp4 ? P.a13[e] : 1.0f;
     };
     auto run = [&](const St &st, int i) {
       const int s = i / Gm::N_GU;
+      const int n_base = (i % Gm::N_GU) * Gm::GU::RP;
       const int *pr = R.pairs + R.offs[s];
-      gate_up_compute<FMT, H, I>(P, st.w, st.alpha, (i % Gm::N_GU) * Gm::GU::RP,
-                                 R.offs[s + 1] - R.offs[s], [pr, k](int j) { return pr[j] / k; },
-                                 [pr](int j) { return pr[j]; }, xl, P.act);
+      const int np = R.offs[s + 1] - R.offs[s];
+      gate_up_compute<FMT, H, I>(P, st.w, st.alpha, np, [pr, k](int j) { return pr[j] / k; }, xl,
+                                 ob);
+      store_results<Gm::GU::RP>(
+          rs_o, lane < np ? (uint32_t)((pr[lane] * I + n_base) * 2) : kOOB, ob);
     };
+    // Two items in flight per wave; ia < ib always (items come out of the
+    // counter in increasing order), so once ib is past the share, so is
+    // every later item.  The unused store between the first loads keeps the
+    // instruction order of the loop.
     St sa, sb;
-    int i = b0;
-    if (i < b1) load(sa, i);
-    while (i < b1) {
-      if (i + 1 < b1) load(sb, i + 1);
+    int ia = take_item(&R.next_b, b0);
+    load(sa, ia);
+    store_results<Gm::GU::RP>(rs_o, kOOB, ob);
+    int ib = take_item(&R.next_b, b0);
+    load(sb, ib);
+    while (ia < b1) {
       __builtin_amdgcn_sched_barrier(0);
-      run(sa, i);
-      if (++i >= b1) break;
-      if (i + 1 < b1) load(sa, i + 1);
+      run(sa, ia);
+      ia = take_item(&R.next_b, b0);
+      load(sa, ia);
+      if (ib >= b1) break;
       __builtin_amdgcn_sched_barrier(0);
-      run(sb, i);
-      ++i;
+      run(sb, ib);
+      ib = take_item(&R.next_b, b0);
+      load(sb, ib);
     }
-    set_flag(&S->gw[gw], P.seq);
+    block_done(&R.done_b, &S->gb[blockIdx.x], P.seq);
   }
   TRACE(P, 4);
 
-  // ---- phase C: blocks [0, n_sdn) shared down; the waves of the other
-  // blocks own routed down items [c0, c1) (wave index gc = gw - sdw; on a
-  // grid too small to set those blocks apart, every wave takes both)
-  const int sdw = 2 * P.n_sdn <= P.nb ? P.n_sdn * kWaves : 0;  // waves kept for shared down
-  const int NWC = NW - sdw;
-  const int gc = gw - sdw;
-  const int QC = max(1, per_wave(R.cum_dn[U], NWC));
+  // ---- phase C: routed down; block share [c0, c1) of equal cost
+  const int QC = max(1, per_wave(R.cum_dn[U], P.nb));
   {
-    const int c0 = gc < 0 ? 0 : first_item(R, R.cum_dn, Gm::N_DN, gc * QC);
-    const int c1 = gc < 0 ? 0 : first_item(R, R.cum_dn, Gm::N_DN, (gc + 1) * QC);
+    const int c0 = first_item(R, R.cum_dn, Gm::N_DN, blockIdx.x * QC);
+    const int c1 = first_item(R, R.cum_dn, Gm::N_DN, (blockIdx.x + 1) * QC);
+    const __amdgpu_buffer_rsrc_t rs_w = make_rsrc(P.w2, (size_t)P.E * H * DN_RSZ);
+    const __amdgpu_buffer_rsrc_t rs_s =
+        make_rsrc(FMT == kNvfp4 ? (const void *)P.s2 : (const void *)P.w2,
+                  FMT == kNvfp4 ? (size_t)P.E * H * (I / 16) : 0);
+    const __amdgpu_buffer_rsrc_t rs_o = make_rsrc(P.y, (size_t)P.M * k * H * 2);
     struct St {
       DownW<FMT, I> w;
       float alpha;
     };
     auto load = [&](St &st, int i) {
-      const int e = R.active[i / Gm::N_DN];
-      down_load(st.w, P.w2 + (size_t)e * H * DN_RSZ,
-                FMT == kNvfp4 ? P.s2 + (size_t)e * H * (I / 16) : nullptr,
-                (i % Gm::N_DN) * Gm::DN::RW);
+      const bool ok = i < c1;
+      const int e = __builtin_amdgcn_readfirstlane(ok ? R.active[i / Gm::N_DN] : 0);
+      down_load(st.w, rs_w, ok ? (uint32_t)e * H * DN_RSZ : kOOB, rs_s,
+                ok ? (uint32_t)e * H * (I / 16) : kOOB, ok ? (i % Gm::N_DN) * Gm::DN::RW : 0);
       st.alpha = FMT == kNvfp4 ? P.a2[e] : 1.0f;
     };
-    St sa, sb;
-    if (c0 < c1) load(sa, c0);
-    if (c0 + 1 < c1) load(sb, c0 + 1);
-    // The staging area is reused below: every wave of the block is done
-    // with x (the first weights are already in flight).
-    __syncthreads();
-    for (int db = blockIdx.x; db < P.n_sdn; db += P.nb) {
-      // shared down: 32 rows, every token (sact staged in groups)
-      const int h_base = db * Gm::SDN_BLOCK + wv * Gm::SDN::RW;
-      DownW<kBf16, I> W;
-      down_load(W, P.sdown, nullptr, h_base);
-      if (wv == 0) wave_wait_flags(S->sg, 0, P.n_sgu, P.seq);
-      constexpr int G = kXLdsBytes / (2 * I) < kMaxDecodeM ? kXLdsBytes / (2 * I) : kMaxDecodeM;
-      for (int g0 = 0; g0 < P.M; g0 += G) {
-        __syncthreads();
-        stage_rows<I, true>(xs, P.sact + (size_t)g0 * I, min(G, P.M - g0));
-        __syncthreads();
-        for (int t = g0; t < min(g0 + G, P.M); ++t)
-          down_one<kBf16, H, I, kSrcLds>(W, xs + (size_t)(t - g0) * I, 1.0f, h_base,
-                                         P.sh + (size_t)t * H);
-      }
-      stores_performed();
-      __syncthreads();
-      if (threadIdx.x == 0) st_dev(&S->sd[db], P.seq);
-    }
-    if (c0 < c1) {
-      // gate/up waves that produced act of this wave's experts
-      const int s_lo = c0 / Gm::N_DN, s_hi = (c1 - 1) / Gm::N_DN;
-      const int w_lo = owner(R, R.cum_gu, s_lo, 0, QB);
-      const int w_hi = owner(R, R.cum_gu, s_hi, Gm::N_GU - 1, QB);
-      wave_wait_flags(S->gw, w_lo, w_hi + 1, P.seq);
-    }
-    TRACE(P, 5);
-    // The activations of the current expert's first pairs are copied to a
-    // slice of the staging area (x is no longer needed) when the expert
-    // changes, so the item loop reads them from LDS and only weight loads
-    // are in flight between items.
-    constexpr int kCache = (kXLdsBytes / kWaves) / (2 * I);  // rows per wave
+    // The first time a wave meets an expert it waits for the blocks owning
+    // that expert's gate/up items, then copies the activations of the
+    // expert's first pairs into its LDS slice, so the item loop reads them
+    // from LDS and only weight loads are in flight between items.
+    constexpr int kCache = (kSliceBytes - Gm::OUT_BYTES) / (2 * I);  // rows per slice
     static_assert(kCache >= 1, "activation cache");
-    uint16_t *ac = xs + (size_t)wv * (kXLdsBytes / kWaves / 2);
     int cur = -1;
     auto run = [&](const St &st, int i) {
       const int s = i / Gm::N_DN;
@@ -642,31 +954,40 @@ decode_kernel(Params P) {
       const int nc = np < kCache ? np : kCache;
       if (s != cur) {
         cur = s;
+        wave_wait_flags(S->gb, owner_block(R, R.cum_gu, s, 0, QB, P.nb),
+                        owner_block(R, R.cum_gu, s, Gm::N_GU - 1, QB, P.nb) + 1, P.seq);
         for (int j = 0; j < nc; ++j)
-          copy_to_lds<true>(ac + (size_t)j * I, P.act + (size_t)pr[j] * I, I / 8, 0, 1);
+          copy_to_lds<true>(slice + (size_t)j * I, P.act + (size_t)pr[j] * I, I / 8, 0, 1);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
       for (int j = 0; j < nc; ++j)
-        down_one<FMT, H, I, kSrcLds>(st.w, ac + (size_t)j * I, st.alpha, h_base,
-                                     P.y + (size_t)pr[j] * H);
+        down_one<FMT, H, I, kSrcLds>(st.w, slice + (size_t)j * I, st.alpha, j, ob);
       for (int j = nc; j < np; ++j)
-        down_one<FMT, H, I, kSrcDevice>(st.w, P.act + (size_t)pr[j] * I, st.alpha, h_base,
-                                        P.y + (size_t)pr[j] * H);
+        down_one<FMT, H, I, kSrcDevice>(st.w, P.act + (size_t)pr[j] * I, st.alpha, j, ob);
+      store_results<Gm::DN::RW>(
+          rs_o, lane < np ? (uint32_t)((pr[lane] * H + h_base) * 2) : kOOB, ob);
     };
-    int i = c0;
-    while (i < c1) {
+    St sa, sb;
+    int ia = take_item(&R.next_c, c0);
+    load(sa, ia);
+    store_results<Gm::DN::RW>(rs_o, kOOB, ob);
+    int ib = take_item(&R.next_c, c0);
+    load(sb, ib);
+    TRACE(P, 5);
+    while (ia < c1) {
       __builtin_amdgcn_sched_barrier(0);
-      run(sa, i);
-      if (i + 2 < c1) load(sa, i + 2);
-      if (++i >= c1) break;
+      run(sa, ia);
+      ia = take_item(&R.next_c, c0);
+      load(sa, ia);
+      if (ib >= c1) break;
       __builtin_amdgcn_sched_barrier(0);
-      run(sb, i);
-      if (i + 2 < c1) load(sb, i + 2);
-      ++i;
+      run(sb, ib);
+      ib = take_item(&R.next_c, c0);
+      load(sb, ib);
     }
-    if (gc >= 0) set_flag(&S->dw[gc], P.seq);
+    block_done(&R.done_c, &S->db[blockIdx.x], P.seq);
   }
   TRACE(P, 6);
 
@@ -676,16 +997,19 @@ decode_kernel(Params P) {
   for (int cb = (NW >= NCB) ? (gw % stride == 0 ? gw / stride : NCB) : gw; cb < NCB;
        cb += (NW >= NCB) ? NCB : NW) {
     const int h0 = cb * Gm::CB;
-    // routed down items of rows [h0, h0 + CB) for every slot
-    constexpr int IPB = Gm::CB / Gm::DN::RW;  // down items per combine block
+    // blocks owning the routed down items of rows [h0, h0 + CB), every slot
+    constexpr int IPB = Gm::CB / Gm::DN::RW;  // down items per combine item
     for (int it = 0, nap = 1; it < (1 << 20); ++it) {
       bool ok = true;
       for (int s = lane; s < U; s += kWave) {
         const int j0 = h0 / Gm::DN::RW;
-        const int w_hi = owner(R, R.cum_dn, s, j0 + IPB - 1, QC);
-        for (int w = owner(R, R.cum_dn, s, j0, QC); w <= w_hi; ++w) ok &= ld_dev(&S->dw[w]) == P.seq;
+        const int b_hi = owner_block(R, R.cum_dn, s, j0 + IPB - 1, QC, P.nb);
+        for (int b = owner_block(R, R.cum_dn, s, j0, QC, P.nb); b <= b_hi; ++b)
+          ok &= ld_dev(&S->db[b]) == P.seq;
       }
-      if (P.sgu && lane == 0) ok &= ld_dev(&S->sd[cb]) == P.seq;
+      if (P.sgu)  // blocks holding the shared down items of these rows
+        for (int j = h0 / Gm::SDN::RW + lane; j < (h0 + Gm::CB) / Gm::SDN::RW; j += kWave)
+          ok &= ld_dev(&S->sd[sh0 + j % nbs]) == P.seq;
       if (__all(ok)) break;
       for (int z = 0; z < nap; ++z) __builtin_amdgcn_s_sleep(2);
       nap = nap < 4 ? nap * 2 : 4;
@@ -693,8 +1017,8 @@ decode_kernel(Params P) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     // y of the rows for a group of tokens is gathered into this wave's LDS
     // slice with direct loads (one round trip per group), then summed.
-    uint16_t *yl = xs + (size_t)wv * (kXLdsBytes / kWaves / 2);
-    constexpr int SLICE = kXLdsBytes / kWaves / 2;  // bf16 per slice
+    uint16_t *yl = slice;
+    constexpr int SLICE = kSliceBytes / 2;  // bf16 per slice
     // tokens per group: at most 4 outputs and 4 gathered chunks per lane
     const int G = min(4 * kWave / Gm::CB, SLICE / (k * Gm::CB));
     for (int t0 = 0; t0 < P.M; t0 += (G > 0 ? G : 1)) {
@@ -749,6 +1073,7 @@ decode_kernel(Params P) {
     }
   }
   TRACE(P, 7);
+  TRACE_FLUSH(P);
 }
 
 struct GridInfo {
@@ -763,17 +1088,15 @@ hipError_t launch(Params P, hipStream_t st) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  static_assert(kRouteTokens8 * H * 2 <= kXLdsBytes, "routing group staging");
-  const bool x_all = P.M * H * 2 <= kXLdsBytes;
-  // The staging area holds all of x (small batches) or one routing group,
-  // and later the activations the down items read.
-  const size_t lds = kXLdsBytes;
+  // The staging area holds all of x (small batches), one routing group or a
+  // group of shared activations; the per-wave slices follow it.
+  const size_t lds = kXLdsBytes + kCacheLdsBytes;
   GridInfo &gi = info[dev];
   if (gi.nb == 0) {
-    // Blocks resident at once with the largest staging area: the grid.
+    // Blocks resident at once: the grid (one block per compute unit).
     int per_cu = 0, cus = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<FMT, H, I>, kThreads,
-                                                     kXLdsBytes);
+                                                     lds);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
@@ -782,13 +1105,11 @@ hipError_t launch(Params P, hipStream_t st) {
     if (gi.nb > kMaxDecodeBlocks) gi.nb = kMaxDecodeBlocks;
   }
   P.nb = gi.nb;
-  const int nEG = (P.E + kWaves - 1) / kWaves;
-  const int nTG = (P.M + kRouteTokens8 - 1) / kRouteTokens8;
-  P.n_route = P.ids_in ? 0 : nEG * nTG;
-  P.n_sgu = P.sgu ? I / Gm::SGU_BLOCK : 0;
-  P.n_sdn = P.sgu ? H / Gm::SDN_BLOCK : 0;
-  if (P.n_sgu > kMaxSharedBlocks || P.n_sdn > kMaxSharedBlocks || P.n_route > kMaxRouteBlocks)
-    return hipErrorInvalidValue;
+  const int nTG = (P.M + kRouteTokens - 1) / kRouteTokens;
+  P.n_route = P.ids_in ? 0 : P.E * nTG;  // routing items (expert, token group)
+  P.n_sgu = P.sgu ? I / Gm::SGU::RP : 0;  // shared gate/up items (row pairs)
+  P.n_sdn = P.sgu ? H / Gm::SDN::RW : 0;  // shared down items
+  if (P.nb > kMaxSharedBlocks) return hipErrorInvalidValue;
   hipLaunchKernelGGL((decode_kernel<FMT, H, I>), dim3(P.nb), dim3(kThreads), lds, st, P);
   return hipGetLastError();
 }
@@ -814,6 +1135,7 @@ hipError_t launch_decode(int fmt, const DecodeArgs &a, hipStream_t st) {
   P.ids_in = a.ids_in;
   P.tw_in = a.tw_in;
   P.logits = a.logits;
+  P.tlog = a.tlog;
   P.ids = a.ids;
   P.tw = a.tw;
   P.act = a.act;

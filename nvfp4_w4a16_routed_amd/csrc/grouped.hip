@@ -69,12 +69,6 @@ struct GemmArgs {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
-// Buffer descriptor of `bytes` bytes at p (raw, untyped; word 3 as the
-// gfx9-family raw buffer loads expect).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, size_t bytes) {
-  const int n = bytes > 0x7fffffffu ? 0x7fffffff : (int)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, n, 0x00020000);
-}
 __device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
 
 // LDS position (in 16-byte chunks) of chunk c of tile row r.  The XOR

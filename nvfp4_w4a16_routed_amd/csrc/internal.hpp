@@ -16,21 +16,19 @@ constexpr int kRouteExperts = 4;
 constexpr int kMaxDecodePairs = 512;
 constexpr int kMaxExperts = 256;
 constexpr int kMaxDecodeM = 64;
-// Decode kernel grid limits: blocks, waves, routing blocks, and the blocks
-// of its shared gate/up and shared down segments.
+// Decode kernel grid limits: blocks, routing blocks, and the blocks of its
+// shared gate/up and shared down segments.
 constexpr int kMaxDecodeBlocks = 1024;
-constexpr int kMaxDecodeWaves = kMaxDecodeBlocks * 8;
 constexpr int kMaxRouteBlocks = 256;
 constexpr int kMaxSharedBlocks = 1024;
 // Completion flags of the decode kernel.  A flag holds the sequence number
 // of the call that set it (every call gets a new one), so flags never need
 // resetting.
 struct DecodeSync {
-  int go[kMaxDecodeBlocks][kMaxRouteBlocks];  // [block][routing block]: logits written
-  int sg[kMaxSharedBlocks];                   // shared gate/up block done
-  int sd[kMaxSharedBlocks];                   // shared down block done
-  int gw[kMaxDecodeWaves];                    // routed gate/up wave done
-  int dw[kMaxDecodeWaves];                    // routed down wave done
+  int sg[kMaxSharedBlocks];  // shared gate/up block done
+  int sd[kMaxSharedBlocks];  // shared down block done
+  int gb[kMaxDecodeBlocks];  // the block's routed gate/up items done
+  int db[kMaxDecodeBlocks];  // the block's routed down items done
 };
 
 // The route kernel's arrival counters follow the decode block: token groups
@@ -50,6 +48,7 @@ struct DecodeArgs {
   const int32_t *ids_in;        // forced routing, NULL = route
   const float *tw_in;
   uint16_t *logits;
+  unsigned long long *tlog;     // [M, E] logits tagged with the call's sequence number
   int32_t *ids;
   float *tw;
   uint16_t *act, *y, *sact, *sh, *out;
@@ -75,6 +74,7 @@ struct Workspace {
   DecodeSync *sync;         // zero between calls
   int32_t *route_counters;  // [kRouteCounterWords], zero between calls
   uint16_t *logits;    // [M, E]
+  unsigned long long *tlog;  // [M, E] decode: tagged logits
   int32_t *ids;        // [M, k]
   float *tw;           // [M, k]
   Plan plan;

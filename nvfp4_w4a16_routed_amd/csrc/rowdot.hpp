@@ -58,19 +58,24 @@ struct VecChunk {
   u32x4_t v[U4];
 };
 
+// One row's chunks for lane q: codes (or bf16 values) at byte offset woff of
+// descriptor w, NVFP4 scales at soff of descriptor s.  Every load is issued
+// (idle lanes and rows past a share read out of range, which returns zero
+// and costs no memory traffic), so the number of loads never varies.
 template <int FMT, int K>
-__device__ __forceinline__ void load_row(RowRegs<FMT, K> &r, const uint8_t *wrow,
-                                         const uint8_t *srow, int q) {
+__device__ __forceinline__ void load_row(RowRegs<FMT, K> &r, __amdgpu_buffer_rsrc_t w,
+                                         uint32_t woff, __amdgpu_buffer_rsrc_t s, uint32_t soff,
+                                         int q) {
   using Map = RowMap<FMT, K>;
 #pragma unroll
   for (int i = 0; i < Map::CPL; ++i) {
     const int c = q + Map::LPR * i;
-    r.raw[i] = u32x4_t{0, 0, 0, 0};
+    const bool on = Map::active(q, i);
+    r.raw[i] = __builtin_bit_cast(
+        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(w, on ? woff + c * 16 : kOOB, 0, kPolicyStream));
     r.sc[i] = 0;
-    if (Map::active(q, i)) {
-      r.raw[i] = load16_stream(wrow + (size_t)c * 16);
-      if constexpr (FMT == kNvfp4) r.sc[i] = load_u16(srow + (size_t)c * 2);
-    }
+    if constexpr (FMT == kNvfp4)
+      r.sc[i] = __builtin_amdgcn_raw_buffer_load_b16(s, on ? soff + c * 2 : kOOB, 0, 0);
   }
 }
 
@@ -216,20 +221,22 @@ struct GateUpW {
   RowRegs<FMT, H> rows[2 * GateUpGeo<FMT, H>::NSL];
 };
 
+// wexp / sexp: byte offsets of the expert's [2I, ...] codes and scales in
+// descriptors w / s (kOOB: no item, nothing is read).
 template <int FMT, int H, int I>
-__device__ __forceinline__ void gate_up_load(GateUpW<FMT, H, I> &W, const uint8_t *wexp,
-                                             const uint8_t *sexp, int n_base) {
+__device__ __forceinline__ void gate_up_load(GateUpW<FMT, H, I> &W, __amdgpu_buffer_rsrc_t w,
+                                             uint32_t wexp, __amdgpu_buffer_rsrc_t sc,
+                                             uint32_t sexp, int n_base) {
   using Map = RowMap<FMT, H>;
   using Geo = GateUpGeo<FMT, H>;
   const int lane = threadIdx.x & (kWave - 1);
   const int r = lane / Map::LPR, q = lane % Map::LPR;
 #pragma unroll
   for (int s = 0; s < Geo::NSL; ++s) {
-    const int n = n_base + s * Map::RS + r;
-    load_row(W.rows[s], wexp + (size_t)n * Map::ROW_BYTES,
-             FMT == kNvfp4 ? sexp + (size_t)n * (H / 16) : nullptr, q);
-    load_row(W.rows[Geo::NSL + s], wexp + (size_t)(I + n) * Map::ROW_BYTES,
-             FMT == kNvfp4 ? sexp + (size_t)(I + n) * (H / 16) : nullptr, q);
+    const uint32_t n = n_base + s * Map::RS + r;
+    load_row(W.rows[s], w, wexp + n * Map::ROW_BYTES, sc, sexp + n * (H / 16), q);
+    load_row(W.rows[Geo::NSL + s], w, wexp + (I + n) * Map::ROW_BYTES, sc,
+             sexp + (I + n) * (H / 16), q);
   }
 }
 
@@ -240,17 +247,17 @@ struct DownW {
 };
 
 template <int FMT, int I>
-__device__ __forceinline__ void down_load(DownW<FMT, I> &W, const uint8_t *wexp,
-                                          const uint8_t *sexp, int h_base) {
+__device__ __forceinline__ void down_load(DownW<FMT, I> &W, __amdgpu_buffer_rsrc_t w,
+                                          uint32_t wexp, __amdgpu_buffer_rsrc_t sc, uint32_t sexp,
+                                          int h_base) {
   using Map = RowMap<FMT, I>;
   using Geo = DownGeo<FMT, I>;
   const int lane = threadIdx.x & (kWave - 1);
   const int r = lane / Map::LPR, q = lane % Map::LPR;
 #pragma unroll
   for (int s = 0; s < Geo::NSL; ++s) {
-    const int h = h_base + s * Map::RS + r;
-    load_row(W.rows[s], wexp + (size_t)h * Map::ROW_BYTES,
-             FMT == kNvfp4 ? sexp + (size_t)h * (I / 16) : nullptr, q);
+    const uint32_t h = h_base + s * Map::RS + r;
+    load_row(W.rows[s], w, wexp + h * Map::ROW_BYTES, sc, sexp + h * (I / 16), q);
   }
 }
 
