@@ -204,12 +204,16 @@ struct Route {
 };
 
 // Work balance.  Item (s, j) of a phase (slot s, j < N items per slot)
-// costs 2 + np_s units, np_s the pairs of slot s (weight bytes plus the
-// arithmetic of every pair); each wave owns the items whose starting cost
-// falls in its share [w Q, (w + 1) Q) of the total, so a hot expert's items
-// are spread over more waves.
+// costs kItemCost + kPairCost * np_s units, np_s the pairs of slot s: the
+// item's weight bytes, then the arithmetic of each pair, which dominates
+// (measured on MI355X: a pair of a gate/up item costs about three times the
+// item's weight traffic).  Each block owns the items whose starting cost
+// falls in its share [b Q, (b + 1) Q) of the total, so a hot expert's items
+// are spread over more blocks.
+constexpr int kItemCost = 1;
+constexpr int kPairCost = 3;
 __device__ __forceinline__ int item_cost(const Route &R, int s) {
-  return 2 + R.offs[s + 1] - R.offs[s];
+  return kItemCost + kPairCost * (R.offs[s + 1] - R.offs[s]);
 }
 
 // Smallest item (global index s * N + j) whose starting cost is >= x.
@@ -426,7 +430,7 @@ __device__ void build_plan_wave(const Params &P, Route &R) {
     flg[i] = cnt[i] > 0;
     c += cnt[i];
     f += flg[i];
-    u += flg[i] ? 2 + cnt[i] : 0;
+    u += flg[i] ? kItemCost + kPairCost * cnt[i] : 0;
   }
   int base = wave_exclusive_scan(c), slot = wave_exclusive_scan(f);
   int cost = wave_exclusive_scan(u);  // in units of one item per slot
@@ -442,7 +446,7 @@ __device__ void build_plan_wave(const Params &P, Route &R) {
     }
     base += cnt[i];
     slot += flg[i];
-    cost += flg[i] ? 2 + cnt[i] : 0;
+    cost += flg[i] ? kItemCost + kPairCost * cnt[i] : 0;
   }
   if (lane == kWave - 1) {
     R.next_b = R.next_c = R.done_b = R.done_c = 0;

@@ -16,23 +16,16 @@ constexpr int pow2_divisor(int n, int cap) {
   while (p * 2 <= cap && n % (p * 2) == 0) p *= 2;
   return p;
 }
-constexpr int pow2_ceil(int n) {
-  int p = 1;
-  while (p < n) p *= 2;
-  return p;
-}
 
-// Lane mapping of a row.  NVFP4 rows: one chunk per lane on a power-of-two
-// group of lanes (a 24-chunk row, I = 768, uses 24 of 32 lanes; the idle
-// lanes contribute zero), which keeps the per-lane vector slice at 64 bytes.
-// BF16 rows: LPR the largest power-of-two divisor of the chunk count, every
-// lane busy.
+// Lane mapping of a row: LPR, the largest power-of-two divisor of the chunk
+// count (at most 64), lanes share a row and each holds CPL chunks, so every
+// lane is busy (a 24-chunk NVFP4 row, I = 768, is 8 lanes x 3 chunks and a
+// wave covers 8 rows per load).
 template <int FMT, int K>
 struct RowMap {
   static constexpr int CE = FMT == kNvfp4 ? 32 : 8;        // elements per chunk
   static constexpr int NC = K / CE;                          // chunks per row
-  static constexpr int LPR = FMT == kNvfp4 ? (NC >= kWave ? kWave : pow2_ceil(NC))
-                                           : pow2_divisor(NC, kWave);  // lanes per row
+  static constexpr int LPR = pow2_divisor(NC, kWave);        // lanes per row
   static constexpr int CPL = (NC + LPR - 1) / LPR;           // chunks per lane
   static constexpr bool PAD = LPR * CPL != NC;               // some lanes idle
   static constexpr int RS = kWave / LPR;                     // rows per slice
