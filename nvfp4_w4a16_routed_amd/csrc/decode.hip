@@ -862,10 +862,14 @@ decode_kernel(Params P) {
   // ---- phase B: routed gate/up; block share [b0, b1) of equal cost
   //
   // Memory instructions per item are fixed (every load issued, items past
-  // the share read out of range; one store per 16 result bytes), and the
-  // loop keeps them in one order -- [loads of item a] [stores of item b]
-  // [loads of item b] ... -- so the wait for an item's weights never waits
-  // for a store or for the other item's loads.
+  // the share read out of range; one store per 16 result bytes), so the
+  // wait for an item's weights never waits for a store.
+  //
+  // One item in flight per wave: the 16 waves of a CU already keep about
+  // 72 KB of weights in flight per CU (18 MB on the chip), enough for the
+  // HBM rate, and a deeper queue only lengthens every round trip the
+  // phases after it wait on (measured on MI355X: two items per wave were
+  // slower end to end).
   const int QB = max(1, per_wave(R.cum_gu[U], P.nb));
   {
     const int b0 = first_item(R, R.cum_gu, Gm::N_GU, blockIdx.x * QB);
@@ -897,26 +901,16 @@ decode_kernel(Params P) {
       store_results<Gm::GU::RP>(
           rs_o, lane < np ? (uint32_t)((pr[lane] * I + n_base) * 2) : kOOB, ob);
     };
-    // Two items in flight per wave; ia < ib always (items come out of the
-    // counter in increasing order), so once ib is past the share, so is
-    // every later item.  The unused store between the first loads keeps the
-    // instruction order of the loop.
-    St sa, sb;
+    // Items come out of the counter in increasing order: the first past the
+    // share ends the wave's part.
+    St sa;
     int ia = take_item(&R.next_b, b0);
     load(sa, ia);
-    store_results<Gm::GU::RP>(rs_o, kOOB, ob);
-    int ib = take_item(&R.next_b, b0);
-    load(sb, ib);
     while (ia < b1) {
       __builtin_amdgcn_sched_barrier(0);
       run(sa, ia);
       ia = take_item(&R.next_b, b0);
       load(sa, ia);
-      if (ib >= b1) break;
-      __builtin_amdgcn_sched_barrier(0);
-      run(sb, ib);
-      ib = take_item(&R.next_b, b0);
-      load(sb, ib);
     }
     block_done(&R.done_b, &S->gb[blockIdx.x], P.seq);
   }
@@ -973,23 +967,15 @@ decode_kernel(Params P) {
       store_results<Gm::DN::RW>(
           rs_o, lane < np ? (uint32_t)((pr[lane] * H + h_base) * 2) : kOOB, ob);
     };
-    St sa, sb;
+    St sa;
     int ia = take_item(&R.next_c, c0);
     load(sa, ia);
-    store_results<Gm::DN::RW>(rs_o, kOOB, ob);
-    int ib = take_item(&R.next_c, c0);
-    load(sb, ib);
     TRACE(P, 5);
     while (ia < c1) {
       __builtin_amdgcn_sched_barrier(0);
       run(sa, ia);
       ia = take_item(&R.next_c, c0);
       load(sa, ia);
-      if (ib >= c1) break;
-      __builtin_amdgcn_sched_barrier(0);
-      run(sb, ib);
-      ib = take_item(&R.next_c, c0);
-      load(sb, ib);
     }
     block_done(&R.done_c, &S->db[blockIdx.x], P.seq);
   }
@@ -1001,19 +987,33 @@ decode_kernel(Params P) {
   for (int cb = (NW >= NCB) ? (gw % stride == 0 ? gw / stride : NCB) : gw; cb < NCB;
        cb += (NW >= NCB) ? NCB : NW) {
     const int h0 = cb * Gm::CB;
-    // blocks owning the routed down items of rows [h0, h0 + CB), every slot
+    // The blocks holding the shared down items of these rows (done long
+    // before the routed ones), then those owning the routed down items of
+    // rows [h0, h0 + CB) of every slot.  Every poll issues all its loads
+    // before comparing any (one round trip): a chunk's items lie in at most
+    // two blocks' shares when a share holds IPB items or more (the blocks
+    // between the two ends are read one by one otherwise).
+    if (P.sgu)
+      for (int it = 0, nap = 1; it < (1 << 20); ++it) {
+        bool ok = true;
+        for (int j = h0 / Gm::SDN::RW + lane; j < (h0 + Gm::CB) / Gm::SDN::RW; j += kWave)
+          ok &= ld_dev(&S->sd[sh0 + j % nbs]) == P.seq;
+        if (__all(ok)) break;
+        for (int z = 0; z < nap; ++z) __builtin_amdgcn_s_sleep(2);
+        nap = nap < 4 ? nap * 2 : 4;
+      }
     constexpr int IPB = Gm::CB / Gm::DN::RW;  // down items per combine item
     for (int it = 0, nap = 1; it < (1 << 20); ++it) {
       bool ok = true;
-      for (int s = lane; s < U; s += kWave) {
+      for (int s0 = 0; s0 < U; s0 += kWave) {
+        const int s = s0 + lane < U ? s0 + lane : U - 1;
         const int j0 = h0 / Gm::DN::RW;
+        const int b_lo = owner_block(R, R.cum_dn, s, j0, QC, P.nb);
         const int b_hi = owner_block(R, R.cum_dn, s, j0 + IPB - 1, QC, P.nb);
-        for (int b = owner_block(R, R.cum_dn, s, j0, QC, P.nb); b <= b_hi; ++b)
-          ok &= ld_dev(&S->db[b]) == P.seq;
+        const int f0 = ld_dev(&S->db[b_lo]), f1 = ld_dev(&S->db[b_hi]);
+        ok &= f0 == P.seq && f1 == P.seq;
+        for (int b = b_lo + 1; b < b_hi; ++b) ok &= ld_dev(&S->db[b]) == P.seq;
       }
-      if (P.sgu)  // blocks holding the shared down items of these rows
-        for (int j = h0 / Gm::SDN::RW + lane; j < (h0 + Gm::CB) / Gm::SDN::RW; j += kWave)
-          ok &= ld_dev(&S->sd[sh0 + j % nbs]) == P.seq;
       if (__all(ok)) break;
       for (int z = 0; z < nap; ++z) __builtin_amdgcn_s_sleep(2);
       nap = nap < 4 ? nap * 2 : 4;
@@ -1041,11 +1041,16 @@ decode_kernel(Params P) {
                 kCachePolicyDevice);
           }
         }
+        if (P.sgu) {
+          // every lane loads (an address in range) with the gathers
+          uint16_t sv[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int o = u * kWave + lane;
-          if (P.sgu && o < nt * Gm::CB)
-            shv[u] = bf16_to_f32(ld_dev(&P.sh[(size_t)(t0 + o / Gm::CB) * H + h0 + o % Gm::CB]));
+          for (int u = 0; u < 4; ++u) {
+            const int o = min(u * kWave + lane, nt * Gm::CB - 1);
+            sv[u] = ld_dev(&P.sh[(size_t)(t0 + o / Gm::CB) * H + h0 + o % Gm::CB]);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) shv[u] = bf16_to_f32(sv[u]);
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): y is in LDS
 #pragma unroll
