@@ -490,14 +490,15 @@ __device__ __forceinline__ void wait_plan(Route &R) {
 
 // --------------------------------------------------------- phase A items
 
-// Copies n 16-byte chunks from global memory straight into LDS (direct
-// loads: no registers, every load in flight at once), by waves
-// wave, wave + nwaves, ... (each moves 1 KB blocks), then waits until the
+// Issues the copy of n 16-byte chunks from global memory straight into LDS
+// (direct loads: no registers, every load in flight at once), by waves
+// wave, wave + nwaves, ... (each moves 1 KB blocks).  DEVICE: device-scope
+// loads of data other blocks wrote.  copy_to_lds then waits until the
 // calling wave's copies have landed (this also waits for its other
-// outstanding loads).  DEVICE: device-scope loads of data other blocks wrote.
+// outstanding loads).
 template <bool DEVICE>
-__device__ __forceinline__ void copy_to_lds(uint16_t *dst, const uint16_t *src, int n, int wave,
-                                            int nwaves) {
+__device__ __forceinline__ void issue_copy_to_lds(uint16_t *dst, const uint16_t *src, int n,
+                                                  int wave, int nwaves) {
   const int lane = lane_id();
   for (int b = wave; b * kWave < n; b += nwaves) {
     const int i = b * kWave + lane;
@@ -506,6 +507,11 @@ __device__ __forceinline__ void copy_to_lds(uint16_t *dst, const uint16_t *src, 
                                        (__attribute__((address_space(3))) void *)(dst + (size_t)b * 512),
                                        16, 0, DEVICE ? kCachePolicyDevice : 0);
   }
+}
+template <bool DEVICE>
+__device__ __forceinline__ void copy_to_lds(uint16_t *dst, const uint16_t *src, int n, int wave,
+                                            int nwaves) {
+  issue_copy_to_lds<DEVICE>(dst, src, n, wave, nwaves);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the copies are in LDS
 }
 
@@ -941,8 +947,13 @@ decode_kernel(Params P) {
     // that expert's gate/up items, then copies the activations of the
     // expert's first pairs into its LDS slice, so the item loop reads them
     // from LDS and only weight loads are in flight between items.
+    // Rows past the slice go to the wave's part of the x staging area once
+    // every wave of the block is past its gate/up items (the only readers
+    // of x there); any further rows are read from global memory per use.
     constexpr int kCache = (kSliceBytes - Gm::OUT_BYTES) / (2 * I);  // rows per slice
+    constexpr int kCacheX = kXLdsBytes / kWaves / (2 * I);           // rows in the x area
     static_assert(kCache >= 1, "activation cache");
+    uint16_t *xpart = xs + (size_t)wv * (kXLdsBytes / kWaves / 2);
     int cur = -1;
     auto run = [&](const St &st, int i) {
       const int s = i / Gm::N_DN;
@@ -950,19 +961,25 @@ decode_kernel(Params P) {
       const int *pr = R.pairs + R.offs[s];
       const int np = R.offs[s + 1] - R.offs[s];
       const int nc = np < kCache ? np : kCache;
+      const int nx = np - nc < kCacheX ? np - nc : kCacheX;
       if (s != cur) {
         cur = s;
         wave_wait_flags(S->gb, owner_block(R, R.cum_gu, s, 0, QB, P.nb),
                         owner_block(R, R.cum_gu, s, Gm::N_GU - 1, QB, P.nb) + 1, P.seq);
-        for (int j = 0; j < nc; ++j)
-          copy_to_lds<true>(slice + (size_t)j * I, P.act + (size_t)pr[j] * I, I / 8, 0, 1);
+        if (nx > 0) wait_lds_at_least(&R.done_b, kWaves);
+        for (int j = 0; j < nc + nx; ++j)  // every row's copies in flight at once
+          issue_copy_to_lds<true>(j < nc ? slice + (size_t)j * I : xpart + (size_t)(j - nc) * I,
+                                  P.act + (size_t)pr[j] * I, I / 8, 0, 1);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the rows are in LDS
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
       for (int j = 0; j < nc; ++j)
         down_one<FMT, H, I, kSrcLds>(st.w, slice + (size_t)j * I, st.alpha, j, ob);
-      for (int j = nc; j < np; ++j)
+      for (int j = 0; j < nx; ++j)
+        down_one<FMT, H, I, kSrcLds>(st.w, xpart + (size_t)j * I, st.alpha, nc + j, ob);
+      for (int j = nc + nx; j < np; ++j)
         down_one<FMT, H, I, kSrcDevice>(st.w, P.act + (size_t)pr[j] * I, st.alpha, j, ob);
       store_results<Gm::DN::RW>(
           rs_o, lane < np ? (uint32_t)((pr[lane] * H + h_base) * 2) : kOOB, ob);
@@ -1053,16 +1070,27 @@ decode_kernel(Params P) {
           for (int u = 0; u < 4; ++u) shv[u] = bf16_to_f32(sv[u]);
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): y is in LDS
+        // The lane's four outputs advance together over the pairs, so their
+        // LDS reads are in flight at once; a dropped id adds +0.
+        double acc[4] = {0.0, 0.0, 0.0, 0.0};  // exact: every product has 16 significant bits
+#pragma unroll 4
+        for (int j = 0; j < k; ++j) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int o = min(u * kWave + lane, nt * Gm::CB - 1);
+            const int tl = o / Gm::CB, hh = o % Gm::CB, p = (t0 + tl) * k + j;
+            float tw = R.tw[p];
+            asm volatile("" : "+v"(tw));  // read for every pair: no branch per pair
+            const float w = (unsigned)R.ids[p] < (unsigned)P.E ? tw : 0.0f;
+            acc[u] += (double)w * (double)bf16_to_f32(yl[(tl * k + j) * Gm::CB + hh]);
+          }
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int o = u * kWave + lane;
           if (o < nt * Gm::CB) {
             const int tl = o / Gm::CB, hh = o % Gm::CB, t = t0 + tl;
-            double acc = 0.0;  // exact: every product has 16 significant bits
-            for (int j = 0; j < k; ++j)
-              if ((unsigned)R.ids[t * k + j] < (unsigned)P.E)
-                acc += (double)R.tw[t * k + j] * (double)bf16_to_f32(yl[(tl * k + j) * Gm::CB + hh]);
-            const float routed = round_bf16((float)acc);
+            const float routed = round_bf16((float)acc[u]);
             P.out[(size_t)t * H + h0 + hh] = (uint16_t)f32_to_bf16(routed + shv[u]);
           }
         }
