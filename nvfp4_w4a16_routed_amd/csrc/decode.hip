@@ -212,6 +212,9 @@ struct Route {
 // are spread over more blocks.
 constexpr int kItemCost = 1;
 constexpr int kPairCost = 3;
+// A top_k up to this is selected by repeated wave maxima, a larger one by
+// a bit-by-bit threshold search.
+constexpr int kTopkByMax = 16;
 __device__ __forceinline__ int item_cost(const Route &R, int s) {
   return kItemCost + kPairCost * (R.offs[s + 1] - R.offs[s]);
 }
@@ -285,32 +288,48 @@ __device__ void topk_token(const Params &P, int t, Route &R, int *scratch) {
     for (int i = 0; i < 4; ++i)
       if (valid[i]) P.logits[(size_t)t * E + ee[i]] = (uint16_t)(v[i] & 0xffffu);
   }
-  // the top_k-th largest key: keys are 24-bit, non-negative when valid
-  int thr = 0;
+  // Lanes j < top_k (top_k <= 64 here) get the selected keys, lane j the
+  // (j+1)-th largest (0 = largest = first in the pages' order).
+  int key = -1;
+  if (k <= kTopkByMax) {
+    // k rounds of a wave maximum (keys are unique): the short dependent
+    // chain of a small top_k
+    for (int r = 0; r < k; ++r) {
+      const int m = wave_max_i32(max(max(keys[0], keys[1]), max(keys[2], keys[3])));
 #pragma unroll
-  for (int bit = 23; bit >= 0; --bit) {
-    const int cand = thr | (1 << bit);
-    const int cnt = __popcll(__ballot(keys[0] >= cand)) + __popcll(__ballot(keys[1] >= cand)) +
-                    __popcll(__ballot(keys[2] >= cand)) + __popcll(__ballot(keys[3] >= cand));
-    thr = cnt >= k ? cand : thr;
-  }
-  // compact the selected keys into scratch[0 .. k)
-  int base = 0;
+      for (int i = 0; i < 4; ++i) keys[i] = keys[i] == m ? -1 : keys[i];
+      key = lane == r ? m : key;
+    }
+  } else {
+    // the top_k-th largest key (keys are 24-bit, non-negative when valid),
+    // bit by bit from the top with ballot counts
+    int thr = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bool sel = keys[i] >= thr;
-    const unsigned long long m = __ballot(sel);
-    if (sel) scratch[base + __popcll(m & ((1ull << lane) - 1ull))] = keys[i];
-    base += __popcll(m);
+    for (int bit = 23; bit >= 0; --bit) {
+      const int cand = thr | (1 << bit);
+      const int cnt = __popcll(__ballot(keys[0] >= cand)) + __popcll(__ballot(keys[1] >= cand)) +
+                      __popcll(__ballot(keys[2] >= cand)) + __popcll(__ballot(keys[3] >= cand));
+      thr = cnt >= k ? cand : thr;
+    }
+    // compact the selected keys into scratch[0 .. k), then rank them
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool sel = keys[i] >= thr;
+      const unsigned long long m = __ballot(sel);
+      if (sel) scratch[base + __popcll(m & ((1ull << lane) - 1ull))] = keys[i];
+      base += __popcll(m);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int ck = lane < k ? scratch[lane] : -1;
+    int rank = 0;
+    for (int j = 0; j < k; ++j) rank += __builtin_amdgcn_readlane(ck, j) > ck;
+    // lane rank takes key ck
+    key = __builtin_amdgcn_ds_permute(rank * 4, ck);
+    key = lane < k ? key : -1;
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // lanes j < top_k (top_k <= 64 here): a selected key, its rank among the
-  // selected (0 = largest = first in the pages' order) and its score
-  const int key = lane < k ? scratch[lane] : -1;
-  int rank = 0;
-  for (int j = 0; j < k; ++j) rank += __builtin_amdgcn_readlane(key, j) > key;
   float sc = 0.0f;
   if (lane < k) {
     const float l = bf16_to_f32(key_bits(key));
@@ -320,15 +339,13 @@ __device__ void topk_token(const Params &P, int t, Route &R, int *scratch) {
   }
   // the fp32 sum of the scores in selection order, one addition at a time
   float S = 0.0f;
-  for (int r = 0; r < k; ++r) {
-    const int src = __builtin_ctzll(__ballot(rank == r && lane < k));
-    S = S + __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc), src));
-  }
+  for (int r = 0; r < k; ++r)
+    S = S + __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc), r));
   const float D = S + 1e-20f;
   if (lane < k) {
     const int e = E - 1 - (key & 0xff);
-    R.ids[t * k + rank] = e;
-    R.tw[t * k + rank] = round_bf16(sc / D);
+    R.ids[t * k + lane] = e;
+    R.tw[t * k + lane] = round_bf16(sc / D);
     atomicOr(&R.tokmask[e], 1ull << t);
   }
 }
@@ -585,13 +602,7 @@ __device__ __forceinline__ void gate_up_compute(const Params &P, const GateUpW<F
   using G = GateUpGeo<FMT, H>;
   const int lane = lane_id();
   const int r = lane / Map::LPR, q = lane % Map::LPR;
-  for (int i = 0; i < np; ++i) {
-    const int t = tok(i);
-    float acc[2 * G::NSL];
-    if (xl)
-      rows_dot<FMT, H, kSrcLds>(W.rows, xl + (size_t)t * H, q, acc);
-    else
-      rows_dot<FMT, H, kSrcGlobal>(W.rows, P.x + (size_t)t * H, q, acc);
+  auto finish = [&](int i, float (&acc)[2 * G::NSL]) {
 #pragma unroll
     for (int s = 0; s < G::NSL; ++s) {
       float gs = group_sum<Map::LPR>(acc[s]);
@@ -603,6 +614,28 @@ __device__ __forceinline__ void gate_up_compute(const Params &P, const GateUpW<F
         }
         ob[i * G::RP + s * Map::RS + r] = (uint16_t)f32_to_bf16(swiglu(gs, us));
       }
+    }
+  };
+  if (xl) {
+    for (int i = 0; i < np; ++i) {
+      float acc[2 * G::NSL];
+      rows_dot<FMT, H, kSrcLds>(W.rows, xl + (size_t)tok(i) * H, q, acc);
+      finish(i, acc);
+    }
+  } else if (np > 0) {
+    // x from global memory: the next vector's part is loaded while this one
+    // is used (one round trip per item instead of one per vector)
+    VecRegs<FMT, H> xa, xb;
+    load_vec<FMT, H, kSrcGlobal>(xa, P.x + (size_t)tok(0) * H, q);
+    for (int i = 0; i < np; i += 2) {
+      load_vec<FMT, H, kSrcGlobal>(xb, P.x + (size_t)tok(i + 1 < np ? i + 1 : i) * H, q);
+      float acc[2 * G::NSL];
+      rows_dot_regs<FMT, H>(W.rows, xa, acc);
+      finish(i, acc);
+      if (i + 1 >= np) break;
+      load_vec<FMT, H, kSrcGlobal>(xa, P.x + (size_t)tok(i + 2 < np ? i + 2 : i + 1) * H, q);
+      rows_dot_regs<FMT, H>(W.rows, xb, acc);
+      finish(i + 1, acc);
     }
   }
 }
