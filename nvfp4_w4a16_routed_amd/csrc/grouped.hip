@@ -19,6 +19,8 @@
 // rule: global scale, SwiGLU, bf16 rounding; a memory-bound kernel then
 // forms the weighted combine and the shared add.
 //
+// The routed experts' products use routed_gemm_kernel (below); the dense
+// ones (router, shared expert) use gemm_kernel:
 // Tile: 256 rows x 128 columns, K steps of 32; 4 waves, wave w owns rows
 // [64 w, 64 w + 64) and all 128 columns (2 x 4 MFMA tiles of 32 x 32).
 // Tiles go global -> registers (two K steps ahead) -> LDS (two stages, NVFP4
@@ -26,6 +28,8 @@
 // XOR-swizzled so the accesses are spread over the LDS banks.
 #include "common.hpp"
 #include "internal.hpp"
+
+#include <type_traits>
 
 namespace flint {
 
@@ -372,6 +376,299 @@ __global__ void __launch_bounds__(kGThreads, 2) gemm_kernel(GemmArgs g) {
   }
 }
 
+// ---- The routed experts' GEMMs: one wave per SIMD, a 256 x 256 tile.
+//
+// Tile: 256 rows (pairs of one expert) x 256 columns (B rows), K stages of
+// 64.  The block's 256 rows are eight 32-row slices; wave w owns slices w and
+// w + 4 (so a short tile still spreads over every wave) and all 256 columns:
+// 2 x 8 MFMA tiles of 32 x 32, 256 accumulator registers, which is why the
+// kernel runs a single wave per SIMD (the accumulators sit in the AGPRs).
+//  - A (activation rows) is not shared between waves: each lane loads its
+//    rows' 64-byte K slices straight into registers, two stages ahead.
+//  - B (NVFP4) is dequantised by every thread (one column: the stage's 64
+//    values) into LDS, three buffers deep: codes are loaded four stages
+//    ahead and dequantised two stages ahead, one barrier per stage, so the
+//    MFMA operand reads never wait for the barrier.
+//  - Within a stage, operand lane l (row l % 32) holds k = 32 (l / 32) +
+//    8 sub + 0..7 for sub-step sub: a lane's four A chunks of a stage are 64
+//    contiguous bytes of its row.  B is read in the same k order, so every
+//    product pairs equal k (the order of the K sum is not part of the rule).
+//  - The MFMA forms C^T (B is the first operand): a lane then holds four
+//    consecutive output columns of one row, stored as 8 bytes.
+// Slices past the tile's end are skipped: per wave 0, 1 or 2 live slices,
+// each a separately compiled loop.
+constexpr int kRBM = 256;   // tile rows
+constexpr int kRBN = 256;   // tile columns (B rows)
+constexpr int kRBK = 64;    // K per stage
+constexpr int kRStages = 3; // LDS buffers of dequantised B
+
+// 16-byte chunk c (0..7, k = 8c .. 8c + 7 of the stage) of tile column r.
+// Conflict-free for the MFMA reads (16 lanes: 16 consecutive columns, one
+// chunk) and the dequant stores (16 lanes: 16 consecutive columns).
+__device__ __forceinline__ int rswz(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
+
+template <int N>
+using IC = std::integral_constant<int, N>;
+
+template <int MODE>
+__global__ void __launch_bounds__(kGThreads, 1) routed_gemm_kernel(GemmArgs g) {
+  constexpr bool kGU = MODE == kRoutedGateUp;
+  __shared__ u32x4_t Bs[kRStages][kRBN * 8];
+  __shared__ int rowidx[kRBM];  // A row (token or pair) of each tile row
+  __shared__ int outrow[kRBM];  // output row of each tile row, -1 = none
+  __shared__ int tile_info[4];
+
+  const int lane = lane_id(), wv = wave_id();
+  const int colw = kGU ? kRBN / 2 : kRBN;  // output columns per tile
+  const int ntn = (g.ncols + colw - 1) / colw;
+
+  // Tile of this block.  Expert e has ceil(count_e / 256) row tiles, all
+  // full but its last.  Row tiles are ordered by cost: every full tile, then
+  // the partial ones of more than 128 rows (two slices on some wave: a full
+  // tile's time), then those of at most 128 rows (half that), each class in
+  // expert order.  Row tile rt goes to XCD rt % 8 (blocks are dealt to the
+  // XCDs round-robin), where its column tiles run on consecutive blocks and
+  // share that XCD's L2; each XCD takes its tiles costliest first, so the
+  // cheap ones fill the end of the launch.  Blocks past the work exit.
+  for (int i = threadIdx.x; i < g.E; i += kGThreads) rowidx[i] = g.counts[i];
+  __syncthreads();
+  if (wv == 0) {
+    int c4[4], nf[4], nl[4], ns[4], tf = 0, tl = 0, ts = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ee = 4 * lane + i;
+      c4[i] = ee < g.E ? rowidx[ee] : 0;
+      const int rem = c4[i] % kRBM;
+      nf[i] = c4[i] / kRBM;
+      nl[i] = rem > kRBM / 2;
+      ns[i] = rem > 0 && rem <= kRBM / 2;
+      tf += nf[i];
+      tl += nl[i];
+      ts += ns[i];
+    }
+    int pf = tf, pl = tl, ps = ts;  // inclusive prefixes over lanes
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int xf = __shfl_up(pf, o, kWave), xl = __shfl_up(pl, o, kWave), xs = __shfl_up(ps, o, kWave);
+      if (lane >= o) {
+        pf += xf;
+        pl += xl;
+        ps += xs;
+      }
+    }
+    const int TF = __shfl(pf, kWave - 1, kWave), TL = __shfl(pl, kWave - 1, kWave),
+              TS = __shfl(ps, kWave - 1, kWave);
+    const int i8 = blockIdx.x / 8;
+    const int rt = (i8 / ntn) * 8 + blockIdx.x % 8;  // row tile
+    // class of rt and its index within the class
+    const int cls = rt < TF ? 0 : (rt < TF + TL ? 1 : 2);
+    const int j = cls == 0 ? rt : (cls == 1 ? rt - TF : rt - TF - TL);
+    int acc = cls == 0 ? pf - tf : (cls == 1 ? pl - tl : ps - ts);
+    const bool ok = rt < TF + TL + TS;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = cls == 0 ? nf[i] : (cls == 1 ? nl[i] : ns[i]);
+      if (ok && j >= acc && j < acc + n) {
+        const int q = cls == 0 ? j - acc : nf[i];
+        tile_info[0] = 4 * lane + i;
+        tile_info[1] = q * kRBM;
+        tile_info[2] = min(kRBM, c4[i] - q * kRBM);
+        tile_info[3] = i8 % ntn;
+      }
+      acc += n;
+    }
+    if (!ok && lane == 0) tile_info[0] = -1;
+  }
+  __syncthreads();
+  const int e = tile_info[0];
+  if (e < 0) return;
+  const int m0 = tile_info[1], nrows = tile_info[2], nt = tile_info[3];
+  {
+    // rows past the end repeat the first (loaded by no live slice)
+    const int i = threadIdx.x;
+    const int p = g.lists[(size_t)e * g.list_stride + m0 + (i < nrows ? i : 0)];
+    rowidx[i] = kGU ? p / g.top_k : p;
+    outrow[i] = i < nrows ? p : -1;
+  }
+  __syncthreads();
+
+  const int K = g.K, nk = K / kRBK;
+  const int n0 = nt * colw;
+  // B row of this thread's tile column (gate/up: columns 0..127 gate rows
+  // n0 + c, 128..255 the matching up rows I + n0 + c); past the end: row 0.
+  const int tc = threadIdx.x;
+  int brow;
+  if constexpr (kGU) {
+    const int c = n0 + (tc & (kRBN / 2 - 1));
+    brow = c < g.ncols ? (tc < kRBN / 2 ? c : g.I + c) : 0;
+  } else {
+    const int c = n0 + tc;
+    brow = c < g.ncols ? c : 0;
+  }
+  const int ncols_b = kGU ? 2 * g.I : g.ncols;
+  const size_t bexp = (size_t)e * ncols_b;
+  const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(g.a, (size_t)g.a_rows * K * 2);
+  const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(g.b + bexp * (K / 2), (size_t)ncols_b * (K / 2));
+  const __amdgpu_buffer_rsrc_t rs_s = make_rsrc(g.bs + bexp * (K / 16), (size_t)ncols_b * (K / 16));
+  const uint32_t bc_off = (uint32_t)brow * (K / 2), bs_off = (uint32_t)brow * (K / 16);
+
+  // live 32-row slices of this wave: w (m = 0) and w + 4 (m = 1)
+  const int nh = (nrows + 31) / 32;
+  const int nm = (nh > wv) + (nh > wv + 4);
+  const int h = lane >> 5;
+  uint32_t a_off[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+    a_off[m] = (uint32_t)rowidx[32 * (wv + 4 * m) + (lane & 31)] * (uint32_t)(K * 2) + h * 64;
+
+  struct Codes {
+    u32x4_t c0, c1;  // 64 E2M1 codes: k = 0..31, 32..63
+    uint32_t s;      // 4 E4M3 scales, one per 16 k
+  };
+  auto load_codes = [&](Codes &C, int s) {
+    C.c0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_b, bc_off, s * 32, 0));
+    C.c1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_b, bc_off, s * 32 + 16, 0));
+    C.s = __builtin_amdgcn_raw_buffer_load_b32(rs_s, bs_off, s * 4, 0);
+  };
+  // Chunks 2 q and 2 q + 1 (k = 16 q .. 16 q + 15, scale byte q) of this
+  // thread's column into an LDS buffer.
+  auto dequant_pair = [&](u32x4_t *buf, const Codes &C, auto q_c) {
+    constexpr int q = decltype(q_c)::value;
+    const float sc = __builtin_amdgcn_cvt_f32_fp8((int)C.s, q);
+    const u32x4_t &cw = q < 2 ? C.c0 : C.c1;
+    buf[rswz(tc, 2 * q)] = dequant8(cw[2 * (q & 1)], sc);
+    buf[rswz(tc, 2 * q + 1)] = dequant8(cw[2 * (q & 1) + 1], sc);
+  };
+  auto dequant_store = [&](u32x4_t *buf, const Codes &C) {
+    dequant_pair(buf, C, IC<0>{});
+    dequant_pair(buf, C, IC<1>{});
+    dequant_pair(buf, C, IC<2>{});
+    dequant_pair(buf, C, IC<3>{});
+  };
+  const float alpha = g.alpha[e];
+
+  auto run = [&](auto nm_c) {
+    constexpr int NM = decltype(nm_c)::value;
+    constexpr int NA = NM > 0 ? NM : 1;
+    f32x16_t acc[NA][8];
+#pragma unroll
+    for (int m = 0; m < NA; ++m)
+#pragma unroll
+      for (int n = 0; n < 8; ++n)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.0f;
+    u32x4_t A[3][NA][4];
+    Codes C[3];
+    auto load_a_m = [&](u32x4_t (&dst)[4], int m, int s) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        dst[q] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_a, a_off[m], s * (kRBK * 2) + q * 16, 0));
+    };
+    auto load_a = [&](u32x4_t (&dst)[NA][4], int s) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          dst[m][q] = __builtin_bit_cast(
+              u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_a, a_off[m], s * (kRBK * 2) + q * 16, 0));
+    };
+    // Stage s (J = s % 3) computes from LDS buffer J and registers A[J]; the
+    // B tile of s + 1 is already in buffer J + 1 and s + 2's is dequantised
+    // into buffer J + 2 during the stage, so the operand reads run ahead
+    // across the stage's barrier (which only orders the dequant stores of
+    // the next stage after this stage's reads of the buffer they reuse).
+    // Requests: codes of s + 4 and A of s + 2, in the order they are
+    // consumed, so each wait covers only what it needs.  Sub-step q reads
+    // the B operands of the next sub-step (for q = 3: sub-step 0 of s + 1),
+    // runs the MFMAs of q and dequantises a quarter of the codes of s + 2;
+    // scheduling barriers keep each sub-step's work together.  Past the last
+    // stage the loads repeat it and the stores fill a buffer never read.
+    u32x4_t bf[2][8];
+    auto read_b = [&](u32x4_t (&dst)[8], const u32x4_t *buf, int sub) {
+      if constexpr (NM > 0) {
+#pragma unroll
+        for (int n = 0; n < 8; ++n) dst[n] = buf[rswz(32 * n + (lane & 31), 4 * h + sub)];
+      }
+    };
+    auto stage = [&](auto j_c, int s) {
+      constexpr int J = decltype(j_c)::value, J1 = (J + 1) % 3, J2 = (J + 2) % 3;
+      auto sub_step = [&](auto q_c) {
+        constexpr int q = decltype(q_c)::value;
+        // the stage's requests, spread over the first sub-steps
+        if constexpr (q == 0) load_codes(C[J1], min(s + 4, nk - 1));
+        if constexpr (q == 1 && NM > 0) load_a_m(A[J2][0], 0, min(s + 2, nk - 1));
+        if constexpr (q == 2 && NM > 1) load_a_m(A[J2][1], 1, min(s + 2, nk - 1));
+        if constexpr (q < 3) read_b(bf[(q + 1) & 1], Bs[J], q + 1);
+        else read_b(bf[0], Bs[J1], 0);
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int n = 0; n < 8; ++n)
+            acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, bf[q & 1][n]),
+                                                                __builtin_bit_cast(bf16x8_t, A[J][m][q]),
+                                                                acc[m][n], 0, 0, 0);
+        dequant_pair(Bs[J2], C[J2], q_c);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      sub_step(IC<0>{});
+      sub_step(IC<1>{});
+      sub_step(IC<2>{});
+      sub_step(IC<3>{});
+      __syncthreads();
+    };
+
+    // prologue: B tiles 0 and 1 in LDS, codes of 2 and 3 and A of 0 and 1
+    // requested, B operands of stage 0's first sub-step read
+    load_codes(C[0], 0);
+    load_codes(C[1], min(1, nk - 1));
+    load_codes(C[2], min(2, nk - 1));
+    load_a(A[0], 0);
+    load_a(A[1], min(1, nk - 1));
+    dequant_store(Bs[0], C[0]);
+    dequant_store(Bs[1], C[1]);
+    load_codes(C[0], min(3, nk - 1));
+    __syncthreads();
+    read_b(bf[0], Bs[0], 0);
+    int s = 0;
+    for (; s + 3 <= nk; s += 3) {
+      stage(IC<0>{}, s);
+      stage(IC<1>{}, s + 1);
+      stage(IC<2>{}, s + 2);
+    }
+    if (s < nk) stage(IC<0>{}, s);
+    if (s + 1 < nk) stage(IC<1>{}, s + 1);
+
+    // acc[m][n][r]: row 32 (wv + 4 m) + lane % 32, column 32 n + 8 (r / 4) +
+    // 4 (lane / 32) + r % 4 of the tile.
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const int orow = outrow[32 * (wv + 4 * m) + (lane & 31)];
+      if (orow < 0) continue;
+      uint16_t *crow = g.c + (size_t)orow * g.ldc;
+#pragma unroll
+      for (int n = 0; n < (kGU ? 4 : 8); ++n)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int col = n0 + 32 * n + 8 * gq + 4 * h;
+          if (col >= g.ncols) continue;
+          uint32_t v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float o;
+            if constexpr (kGU) o = swiglu(acc[m][n][4 * gq + i] * alpha, acc[m][n + 4][4 * gq + i] * alpha);
+            else o = acc[m][n][4 * gq + i] * alpha;
+            v[i] = f32_to_bf16(o);
+          }
+          *reinterpret_cast<uint2 *>(crow + col) = make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
+        }
+    }
+  };
+  if (nm == 2) run(IC<2>{});
+  else if (nm == 1) run(IC<1>{});
+  else run(IC<0>{});
+}
+
 // out[t, h] = bf16(bf16(sum_j tw[t, j] y[t*k + j, h]) + sh[t, h]) for 8
 // consecutive h per thread: the k rows of y are loaded together (16 bytes
 // each), the sum is exact in fp64 (every product has 16 significant bits)
@@ -449,6 +746,16 @@ hipError_t launch_gemm(const GemmArgs &g, int row_tiles, int col_tiles, hipStrea
   return hipGetLastError();
 }
 
+// Grid: every XCD gets ceil(row_tiles / 8) row tiles' worth of blocks
+// (row_tiles: an upper bound on the actual count, known on the device).
+template <int MODE>
+hipError_t launch_routed(const GemmArgs &g, int row_tiles, int col_tiles, hipStream_t st) {
+  const int nblk = (row_tiles + 7) / 8 * 8 * col_tiles;
+  if (nblk <= 0) return hipSuccess;
+  hipLaunchKernelGGL((routed_gemm_kernel<MODE>), dim3(nblk), dim3(kGThreads), 0, st, g);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool grouped_shape_supported(int H, int I, int SI) {
@@ -501,7 +808,7 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
   }
   // 4. routed gate/up: row tiles bounded by sum_e ceil(count_e / 256)
   if ((err = mark(3)) != hipSuccess) return err;
-  const int max_row_tiles = (P + kBM - 1) / kBM + E;
+  const int max_row_tiles = (P + kRBM - 1) / kRBM + E;
   {
     GemmArgs gu{};
     gu.a = a.x;
@@ -519,7 +826,8 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
     gu.counts = a.counts;
     gu.list_stride = M;
     gu.E = E;
-    if ((err = launch_gemm<kRoutedGateUp>(gu, max_row_tiles, I / (kBN / 2), st)) != hipSuccess)
+    if ((err = launch_routed<kRoutedGateUp>(gu, max_row_tiles, (I + kRBN / 2 - 1) / (kRBN / 2), st)) !=
+        hipSuccess)
       return err;
   }
   // 5. routed down
@@ -540,7 +848,8 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
     dn.counts = a.counts;
     dn.list_stride = M;
     dn.E = E;
-    if ((err = launch_gemm<kRoutedDown>(dn, max_row_tiles, H / kBN, st)) != hipSuccess) return err;
+    if ((err = launch_routed<kRoutedDown>(dn, max_row_tiles, (H + kRBN - 1) / kRBN, st)) != hipSuccess)
+      return err;
   }
   // 6. shared down -> sh
   if ((err = mark(5)) != hipSuccess) return err;
