@@ -27,6 +27,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 
+// Two fp32 -> packed bf16 (a in the low half), round to nearest even, by
+// gfx950's paired converter.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 // fp32 -> nearest bf16 value, kept in fp32.
 __device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
 

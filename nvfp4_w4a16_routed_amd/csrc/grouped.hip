@@ -389,10 +389,9 @@ __global__ void __launch_bounds__(kGThreads, 2) gemm_kernel(GemmArgs g) {
 //    values) into LDS, three buffers deep: codes are loaded four stages
 //    ahead and dequantised two stages ahead, one barrier per stage, so the
 //    MFMA operand reads never wait for the barrier.
-//  - Within a stage, operand lane l (row l % 32) holds k = 32 (l / 32) +
-//    8 sub + 0..7 for sub-step sub: a lane's four A chunks of a stage are 64
-//    contiguous bytes of its row.  B is read in the same k order, so every
-//    product pairs equal k (the order of the K sum is not part of the rule).
+//  - Operand lane l (row l % 32) holds k = 16 sub + 8 (l / 32) + 0..7 of
+//    the stage for sub-step sub (the MFMA's own layout): each A load moves
+//    32 contiguous bytes of each of 32 rows.
 //  - The MFMA forms C^T (B is the first operand): a lane then holds four
 //    consecutive output columns of one row, stored as 8 bytes.
 // Slices past the tile's end are skipped: per wave 0, 1 or 2 live slices,
@@ -413,13 +412,14 @@ using IC = std::integral_constant<int, N>;
 template <int MODE>
 __global__ void __launch_bounds__(kGThreads, 1) routed_gemm_kernel(GemmArgs g) {
   constexpr bool kGU = MODE == kRoutedGateUp;
-  __shared__ u32x4_t Bs[kRStages][kRBN * 8];
+  constexpr int BN = kRBN, NN = BN / 32;  // tile columns, MFMA column tiles
+  __shared__ u32x4_t Bs[kRStages][BN * 8];
   __shared__ int rowidx[kRBM];  // A row (token or pair) of each tile row
   __shared__ int outrow[kRBM];  // output row of each tile row, -1 = none
   __shared__ int tile_info[4];
 
   const int lane = lane_id(), wv = wave_id();
-  const int colw = kGU ? kRBN / 2 : kRBN;  // output columns per tile
+  const int colw = kGU ? BN / 2 : BN;  // output columns per tile
   const int ntn = (g.ncols + colw - 1) / colw;
 
   // Tile of this block.  Expert e has ceil(count_e / 256) row tiles, all
@@ -499,8 +499,8 @@ __global__ void __launch_bounds__(kGThreads, 1) routed_gemm_kernel(GemmArgs g) {
   const int tc = threadIdx.x;
   int brow;
   if constexpr (kGU) {
-    const int c = n0 + (tc & (kRBN / 2 - 1));
-    brow = c < g.ncols ? (tc < kRBN / 2 ? c : g.I + c) : 0;
+    const int c = n0 + (tc & (BN / 2 - 1));
+    brow = c < g.ncols ? (tc < BN / 2 ? c : g.I + c) : 0;
   } else {
     const int c = n0 + tc;
     brow = c < g.ncols ? c : 0;
@@ -519,15 +519,15 @@ __global__ void __launch_bounds__(kGThreads, 1) routed_gemm_kernel(GemmArgs g) {
   uint32_t a_off[2];
 #pragma unroll
   for (int m = 0; m < 2; ++m)
-    a_off[m] = (uint32_t)rowidx[32 * (wv + 4 * m) + (lane & 31)] * (uint32_t)(K * 2) + h * 64;
+    a_off[m] = (uint32_t)rowidx[32 * (wv + 4 * m) + (lane & 31)] * (uint32_t)(K * 2) + h * 16;
 
   struct Codes {
-    u32x4_t c0, c1;  // 64 E2M1 codes: k = 0..31, 32..63
-    uint32_t s;      // 4 E4M3 scales, one per 16 k
+    u32x4_t c[2];  // 64 E2M1 codes: k = 32 i + 0..31
+    uint32_t s;    // 4 E4M3 scales, one per 16 k
   };
   auto load_codes = [&](Codes &C, int s) {
-    C.c0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_b, bc_off, s * 32, 0));
-    C.c1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_b, bc_off, s * 32 + 16, 0));
+    C.c[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_b, bc_off, s * 32, 0));
+    C.c[1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_b, bc_off, s * 32 + 16, 0));
     C.s = __builtin_amdgcn_raw_buffer_load_b32(rs_s, bs_off, s * 4, 0);
   };
   // Chunks 2 q and 2 q + 1 (k = 16 q .. 16 q + 15, scale byte q) of this
@@ -535,7 +535,7 @@ __global__ void __launch_bounds__(kGThreads, 1) routed_gemm_kernel(GemmArgs g) {
   auto dequant_pair = [&](u32x4_t *buf, const Codes &C, auto q_c) {
     constexpr int q = decltype(q_c)::value;
     const float sc = __builtin_amdgcn_cvt_f32_fp8((int)C.s, q);
-    const u32x4_t &cw = q < 2 ? C.c0 : C.c1;
+    const u32x4_t &cw = C.c[q >> 1];
     buf[rswz(tc, 2 * q)] = dequant8(cw[2 * (q & 1)], sc);
     buf[rswz(tc, 2 * q + 1)] = dequant8(cw[2 * (q & 1) + 1], sc);
   };
@@ -550,11 +550,11 @@ __global__ void __launch_bounds__(kGThreads, 1) routed_gemm_kernel(GemmArgs g) {
   auto run = [&](auto nm_c) {
     constexpr int NM = decltype(nm_c)::value;
     constexpr int NA = NM > 0 ? NM : 1;
-    f32x16_t acc[NA][8];
+    f32x16_t acc[NA][NN];
 #pragma unroll
     for (int m = 0; m < NA; ++m)
 #pragma unroll
-      for (int n = 0; n < 8; ++n)
+      for (int n = 0; n < NN; ++n)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.0f;
     u32x4_t A[3][NA][4];
@@ -563,7 +563,7 @@ __global__ void __launch_bounds__(kGThreads, 1) routed_gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         dst[q] = __builtin_bit_cast(
-            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_a, a_off[m], s * (kRBK * 2) + q * 16, 0));
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_a, a_off[m], s * (kRBK * 2) + q * 32, 0));
     };
     auto load_a = [&](u32x4_t (&dst)[NA][4], int s) {
 #pragma unroll
@@ -571,7 +571,7 @@ __global__ void __launch_bounds__(kGThreads, 1) routed_gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           dst[m][q] = __builtin_bit_cast(
-              u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_a, a_off[m], s * (kRBK * 2) + q * 16, 0));
+              u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_a, a_off[m], s * (kRBK * 2) + q * 32, 0));
     };
     // Stage s (J = s % 3) computes from LDS buffer J and registers A[J]; the
     // B tile of s + 1 is already in buffer J + 1 and s + 2's is dequantised
@@ -584,11 +584,11 @@ __global__ void __launch_bounds__(kGThreads, 1) routed_gemm_kernel(GemmArgs g) {
     // runs the MFMAs of q and dequantises a quarter of the codes of s + 2;
     // scheduling barriers keep each sub-step's work together.  Past the last
     // stage the loads repeat it and the stores fill a buffer never read.
-    u32x4_t bf[2][8];
-    auto read_b = [&](u32x4_t (&dst)[8], const u32x4_t *buf, int sub) {
+    u32x4_t bf[2][NN];
+    auto read_b = [&](u32x4_t (&dst)[NN], const u32x4_t *buf, int sub) {
       if constexpr (NM > 0) {
 #pragma unroll
-        for (int n = 0; n < 8; ++n) dst[n] = buf[rswz(32 * n + (lane & 31), 4 * h + sub)];
+        for (int n = 0; n < NN; ++n) dst[n] = buf[rswz(32 * n + (lane & 31), 2 * sub + h)];
       }
     };
     auto stage = [&](auto j_c, int s) {
@@ -604,7 +604,7 @@ __global__ void __launch_bounds__(kGThreads, 1) routed_gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int m = 0; m < NM; ++m)
 #pragma unroll
-          for (int n = 0; n < 8; ++n)
+          for (int n = 0; n < NN; ++n)
             acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, bf[q & 1][n]),
                                                                 __builtin_bit_cast(bf16x8_t, A[J][m][q]),
                                                                 acc[m][n], 0, 0, 0);
@@ -647,26 +647,118 @@ __global__ void __launch_bounds__(kGThreads, 1) routed_gemm_kernel(GemmArgs g) {
       if (orow < 0) continue;
       uint16_t *crow = g.c + (size_t)orow * g.ldc;
 #pragma unroll
-      for (int n = 0; n < (kGU ? 4 : 8); ++n)
+      for (int n = 0; n < (kGU ? NN / 2 : NN); ++n)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
           const int col = n0 + 32 * n + 8 * gq + 4 * h;
           if (col >= g.ncols) continue;
-          uint32_t v[4];
+          float o[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float o;
-            if constexpr (kGU) o = swiglu(acc[m][n][4 * gq + i] * alpha, acc[m][n + 4][4 * gq + i] * alpha);
-            else o = acc[m][n][4 * gq + i] * alpha;
-            v[i] = f32_to_bf16(o);
+            if constexpr (kGU)
+              o[i] = swiglu(acc[m][n][4 * gq + i] * alpha, acc[m][n + NN / 2][4 * gq + i] * alpha);
+            else o[i] = acc[m][n][4 * gq + i] * alpha;
           }
-          *reinterpret_cast<uint2 *>(crow + col) = make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
+          *reinterpret_cast<uint2 *>(crow + col) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
         }
     }
   };
   if (nm == 2) run(IC<2>{});
   else if (nm == 1) run(IC<1>{});
   else run(IC<0>{});
+}
+
+// Router logits of the grouped path: logits[t, c] = bf16(fp32 x[t] . R[c]).
+// A block takes 32 tokens and up to 128 experts (blockIdx.y: which 128) in
+// tiles of 32; its
+// four waves split K into quarters, and the four partial tiles are added in
+// wave order through LDS (a fixed order: the result does not depend on
+// timing).  Both operands go straight from memory into registers, one K
+// chunk of 64 ahead, in the MFMA's own layout (operand lane l: row l % 32,
+// k = 16 sub + 8 (l / 32) + 0..7 for sub-step sub).  The MFMA forms tiles
+// with experts as rows: lane l holds token l % 32.
+constexpr int kRouterTokens = 32;
+
+__global__ void __launch_bounds__(kGThreads, 1) router_kernel(const uint16_t *__restrict__ x,
+                                                              const uint16_t *__restrict__ R, int M, int K,
+                                                              int E, uint16_t *__restrict__ logits) {
+  __shared__ f32x16_t part[3][4][kWave];  // partial tiles of waves 1..3
+  const int lane = lane_id(), wv = wave_id(), h = lane >> 5, r = lane & 31;
+  const int t0 = blockIdx.x * kRouterTokens;
+  const int e0 = blockIdx.y * 128;
+  const int nte = min(4, (E - e0 + 31) / 32);
+  const __amdgpu_buffer_rsrc_t rs_x = make_rsrc(x, (size_t)M * K * 2);
+  const __amdgpu_buffer_rsrc_t rs_r = make_rsrc(R, (size_t)E * K * 2);
+  // this wave's K range: chunks of 64 [c0, c1) (K is a multiple of 64)
+  const int NK = K / 64, c0 = wv * NK / 4, c1 = (wv + 1) * NK / 4;
+  const uint32_t k0 = (uint32_t)(c0 * 128);  // in bytes
+  const uint32_t xo = (uint32_t)min(t0 + r, M - 1) * (uint32_t)(K * 2) + k0 + h * 16;
+  const uint32_t ro = (uint32_t)(e0 + r) * (uint32_t)(K * 2) + k0 + h * 16;  // + 32 j rows
+  const int nk = c1 - c0;
+
+  auto run = [&](auto nt_c) {
+    constexpr int NT = decltype(nt_c)::value;  // expert tiles (E <= 32 NT)
+    f32x16_t acc[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[j][i] = 0.0f;
+    u32x4_t a[2][4], b[2][NT][4];
+    auto load = [&](auto buf_c, int kc) {
+      constexpr int B = decltype(buf_c)::value;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        a[B][q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_x, xo, kc * 128 + q * 32, 0));
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        // rows past E: clamped to row E - 1 (their results are not stored)
+        const uint32_t o = e0 + 32 * j + r < E ? ro + (uint32_t)(32 * j * K * 2) : (uint32_t)(E - 1) * (K * 2) + k0 + h * 16;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          b[B][j][q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_r, o, kc * 128 + q * 32, 0));
+      }
+    };
+    auto mma = [&](auto buf_c) {
+      constexpr int B = decltype(buf_c)::value;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b[B][j][q]),
+                                                           __builtin_bit_cast(bf16x8_t, a[B][q]), acc[j], 0, 0, 0);
+    };
+    load(IC<0>{}, 0);
+    for (int kc = 0; kc < nk; kc += 2) {
+      load(IC<1>{}, min(kc + 1, nk - 1));
+      mma(IC<0>{});
+      load(IC<0>{}, min(kc + 2, nk - 1));  // past the end: a repeat, unused
+      if (kc + 1 < nk) mma(IC<1>{});
+    }
+    if (wv > 0) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) part[wv - 1][j][lane] = acc[j];
+    }
+    __syncthreads();
+    if (wv > 0) return;
+#pragma unroll
+    for (int w = 0; w < 3; ++w)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[j] += part[w][j][lane];
+    // acc[j][i]: expert e0 + 32 j + 8 (i / 4) + 4 h + i % 4, token t0 + r
+    const int t = t0 + r;
+    if (t < M) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int c = e0 + 32 * j + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (c < E) logits[(size_t)t * E + c] = (uint16_t)f32_to_bf16(acc[j][i]);
+        }
+    }
+  };
+  if (nte <= 1) run(IC<1>{});
+  else if (nte <= 2) run(IC<2>{});
+  else run(IC<4>{});
 }
 
 // out[t, h] = bf16(bf16(sum_j tw[t, j] y[t*k + j, h]) + sh[t, h]) for 8
@@ -713,27 +805,56 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint16_t *__restrict
 }
 
 // Pair lists per expert: block e compacts the pairs p (ascending) whose
-// expert is e into lists[e][0 .. count), count into counts[e].
+// expert is e into lists[e][0 .. count), count into counts[e].  The ids are
+// read in chunks of 8192 (coalesced, staged through LDS, the next chunk's
+// loads in flight meanwhile); thread t takes 32 consecutive pairs of a
+// chunk, so an exclusive scan of the per-thread match counts over the block
+// gives every match its slot, in ascending order.
 __global__ void __launch_bounds__(256) plan_lists_kernel(const int32_t *__restrict__ ids, int npairs,
                                                          int32_t *__restrict__ lists, int stride,
                                                          int32_t *__restrict__ counts) {
-  __shared__ int wbase[4];
+  constexpr int kPer = 32, kChunk = 256 * kPer;
+  __shared__ int sid[kChunk];
+  __shared__ int wsum[4];
   const int e = blockIdx.x;
   const int lane = lane_id(), wv = wave_id();
+  int v[kPer];
+  auto fetch = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int p = c0 + i * 256 + (int)threadIdx.x;
+      v[i] = p < npairs ? ids[p] : -1;
+    }
+  };
   int base = 0;
-  for (int p0 = 0; p0 < npairs; p0 += 256) {
-    const int p = p0 + threadIdx.x;
-    const bool hit = p < npairs && ids[p] == e;
-    const uint64_t m = __ballot(hit);
-    if (lane == 0) wbase[wv] = __popcll(m);
+  fetch(0);
+  for (int c0 = 0; c0 < npairs; c0 += kChunk) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) sid[i * 256 + threadIdx.x] = v[i];
     __syncthreads();
-    int off = base;
-    for (int w = 0; w < wv; ++w) off += wbase[w];
-    const int pos = off + __popcll(m & ((1ull << lane) - 1ull));
-    if (hit && pos < stride) lists[(size_t)e * stride + pos] = p;
-    const int tot = wbase[0] + wbase[1] + wbase[2] + wbase[3];
+    fetch(c0 + kChunk);
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) m |= (uint32_t)(sid[threadIdx.x * kPer + j] == e) << j;
+    const int n = __popc(m);
+    int incl = n;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int t = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += t;
+    }
+    if (lane == kWave - 1) wsum[wv] = incl;
     __syncthreads();
-    base += tot;
+    int off = base + incl - n;
+    for (int w = 0; w < wv; ++w) off += wsum[w];
+    base += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    while (m) {
+      const int j = __ffs(m) - 1;
+      m &= m - 1;
+      if (off < stride) lists[(size_t)e * stride + off] = c0 + (int)threadIdx.x * kPer + j;
+      ++off;
+    }
+    __syncthreads();  // sid and wsum are rewritten next chunk
   }
   if (threadIdx.x == 0) counts[e] = min(base, stride);  // an expert has <= 1 pair per token
 }
@@ -749,7 +870,9 @@ hipError_t launch_gemm(const GemmArgs &g, int row_tiles, int col_tiles, hipStrea
 // Grid: every XCD gets ceil(row_tiles / 8) row tiles' worth of blocks
 // (row_tiles: an upper bound on the actual count, known on the device).
 template <int MODE>
-hipError_t launch_routed(const GemmArgs &g, int row_tiles, int col_tiles, hipStream_t st) {
+hipError_t launch_routed(const GemmArgs &g, int row_tiles, hipStream_t st) {
+  const int colw = MODE == kRoutedGateUp ? kRBN / 2 : kRBN;
+  const int col_tiles = (g.ncols + colw - 1) / colw;
   const int nblk = (row_tiles + 7) / 8 * 8 * col_tiles;
   if (nblk <= 0) return hipSuccess;
   hipLaunchKernelGGL((routed_gemm_kernel<MODE>), dim3(nblk), dim3(kGThreads), 0, st, g);
@@ -773,17 +896,10 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
   // 1. router logits and top-k (skipped with forced routing)
   if ((err = mark(0)) != hipSuccess) return err;
   if (!a.ids_in) {
-    GemmArgs r{};
-    r.a = a.x;
-    r.b = reinterpret_cast<const uint8_t *>(a.router);
-    r.c = a.logits;
-    r.rows = M;
-    r.a_rows = M;
-    r.K = H;
-    r.ncols = E;
-    r.ldc = E;
-    if ((err = launch_gemm<kRouter>(r, (M + kBM - 1) / kBM, (E + kBN - 1) / kBN, st)) != hipSuccess)
-      return err;
+    hipLaunchKernelGGL(router_kernel, dim3((M + kRouterTokens - 1) / kRouterTokens, (E + 127) / 128),
+                       dim3(kGThreads), 0, st,
+                       a.x, a.router, M, H, E, a.logits);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
     if ((err = launch_topk(a.logits, M, E, k, a.ids, a.tw, nullptr, st)) != hipSuccess) return err;
   }
   // 2. pair lists per expert
@@ -826,9 +942,7 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
     gu.counts = a.counts;
     gu.list_stride = M;
     gu.E = E;
-    if ((err = launch_routed<kRoutedGateUp>(gu, max_row_tiles, (I + kRBN / 2 - 1) / (kRBN / 2), st)) !=
-        hipSuccess)
-      return err;
+    if ((err = launch_routed<kRoutedGateUp>(gu, max_row_tiles, st)) != hipSuccess) return err;
   }
   // 5. routed down
   if ((err = mark(4)) != hipSuccess) return err;
@@ -848,8 +962,7 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
     dn.counts = a.counts;
     dn.list_stride = M;
     dn.E = E;
-    if ((err = launch_routed<kRoutedDown>(dn, max_row_tiles, (H + kRBN - 1) / kRBN, st)) != hipSuccess)
-      return err;
+    if ((err = launch_routed<kRoutedDown>(dn, max_row_tiles, st)) != hipSuccess) return err;
   }
   // 6. shared down -> sh
   if ((err = mark(5)) != hipSuccess) return err;
