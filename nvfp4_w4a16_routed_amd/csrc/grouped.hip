@@ -73,7 +73,8 @@ struct GemmArgs {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
-__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+// (read from the first lane, so the compiler knows it is uniform in the wave)
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
 
 // LDS position (in 16-byte chunks) of chunk c of tile row r.  The XOR
 // pattern keeps both kinds of access free of bank conflicts: an MFMA operand
@@ -704,18 +705,21 @@ __global__ void __launch_bounds__(kGThreads, 1) router_kernel(const uint16_t *__
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[j][i] = 0.0f;
     u32x4_t a[2][4], b[2][NT][4];
+    // chunk kc's operands; past the wave's range the loads read zeros (an
+    // offset beyond every descriptor), so the MFMAs on them add nothing
     auto load = [&](auto buf_c, int kc) {
       constexpr int B = decltype(buf_c)::value;
+      const uint32_t so = kc < nk ? (uint32_t)(kc * 128) : kOOB;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        a[B][q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_x, xo, kc * 128 + q * 32, 0));
+        a[B][q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_x, xo, so + q * 32, 0));
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         // rows past E: clamped to row E - 1 (their results are not stored)
         const uint32_t o = e0 + 32 * j + r < E ? ro + (uint32_t)(32 * j * K * 2) : (uint32_t)(E - 1) * (K * 2) + k0 + h * 16;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          b[B][j][q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_r, o, kc * 128 + q * 32, 0));
+          b[B][j][q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_r, o, so + q * 32, 0));
       }
     };
     auto mma = [&](auto buf_c) {
@@ -727,12 +731,17 @@ __global__ void __launch_bounds__(kGThreads, 1) router_kernel(const uint16_t *__
           acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b[B][j][q]),
                                                            __builtin_bit_cast(bf16x8_t, a[B][q]), acc[j], 0, 0, 0);
     };
+    // (scheduling barriers keep each chunk's loads ahead of the MFMAs of
+    // the chunk before it)
     load(IC<0>{}, 0);
     for (int kc = 0; kc < nk; kc += 2) {
-      load(IC<1>{}, min(kc + 1, nk - 1));
+      load(IC<1>{}, kc + 1);
+      __builtin_amdgcn_sched_barrier(0);
       mma(IC<0>{});
-      load(IC<0>{}, min(kc + 2, nk - 1));  // past the end: a repeat, unused
-      if (kc + 1 < nk) mma(IC<1>{});
+      __builtin_amdgcn_sched_barrier(0);
+      load(IC<0>{}, kc + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(IC<1>{});
     }
     if (wv > 0) {
 #pragma unroll
