@@ -54,7 +54,7 @@ def _args():
 # with other sources no longer describes the kernel and is ignored.
 KERNEL_SOURCES = {
     "decode_kernel": ["decode.hip", "rowdot.hpp", "common.hpp", "internal.hpp"],
-    "gemm_kernel": ["grouped.hip", "common.hpp", "internal.hpp"],
+    "routed_gemm_kernel": ["grouped.hip", "common.hpp", "internal.hpp"],
 }
 
 
@@ -295,11 +295,11 @@ def main():
     if path == "grouped":
         fl = flops(cfg)
         tfl = fl["gate_up"] / (kern_ms * 1e-3) / 1e12
-        roof = {"kernel": "gemm_kernel<routed gate/up>", "bound": "mfma",
+        roof = {"kernel": "routed_gemm_kernel<gate/up>", "bound": "mfma",
                 "achieved": round(tfl, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tfl / BF16_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic("gemm_kernel_routed_gate_up_m4096_hbm_traffic",
-                                            "gemm_kernel", cfg["name"]),
+                "traffic": measured_traffic("routed_gemm_kernel_gate_up_m4096_hbm_traffic",
+                                            "routed_gemm_kernel", cfg["name"]),
                 "flops_per_launch": fl["gate_up"], "avg_launch_us": round(kern_ms * 1e3, 3)}
     else:
         dom_gbps = nbytes["total"] / (kern_ms * 1e-3) / 1e9
@@ -352,12 +352,12 @@ def main():
             "mfma_frac": round(fl["total"] / (g["ms_step"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "stage_us": {n: round(float(t) * 1e3, 2) for n, t in zip(fm.STAGES, st)},
             "gemm_tflops": {n: round(fl[n] / (gemm_ms[n] * 1e-3) / 1e12, 1) for n in gemm_ms},
-            "roofline": {"kernel": "gemm_kernel<routed gate/up>", "bound": "mfma",
+            "roofline": {"kernel": "routed_gemm_kernel<gate/up>", "bound": "mfma",
                          "achieved": round(fl["gate_up"] / (st[3] * 1e-3) / 1e12, 1),
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(fl["gate_up"] / (st[3] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                         "traffic": measured_traffic("gemm_kernel_routed_gate_up_m4096_hbm_traffic",
-                                                     "gemm_kernel", gc["name"]),
+                         "traffic": measured_traffic("routed_gemm_kernel_gate_up_m4096_hbm_traffic",
+                                                     "routed_gemm_kernel", gc["name"]),
                          "flops_per_launch": fl["gate_up"], "avg_launch_us": round(st[3] * 1e3, 2)},
         }
     print(json.dumps(res), flush=True)

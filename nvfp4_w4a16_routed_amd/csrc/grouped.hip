@@ -10,22 +10,22 @@
 //   shared: sact = bf16(silu(xWg) * xWu), sh = bf16(sact . Wd)   (fp32 sums)
 //   out[t, h] = bf16(bf16(sum_j tw[t, j] y[t*k + j, h]) + sh[t, h])
 //
-// One GEMM kernel, C[rows, cols] = A[rows, K] . B[cols, K]^T, serves every
-// product: the router, the shared expert's gate/up and down, and the routed
-// experts' gate/up and down with A rows gathered through each expert's pair
-// list.  NVFP4 B tiles are dequantised exactly (E2M1 value times its E4M3
-// block scale, in fp32, then to bf16) into LDS; every product is a bf16 MFMA
-// (v_mfma_f32_32x32x16_bf16) with fp32 accumulation.  Epilogues apply the
-// rule: global scale, SwiGLU, bf16 rounding; a memory-bound kernel then
-// forms the weighted combine and the shared add.
+// Every product is C[rows, cols] = A[rows, K] . B[cols, K]^T on bf16 MFMAs
+// (v_mfma_f32_32x32x16_bf16) with fp32 accumulation:
+//  - router_kernel: the router logits (then topk_kernel);
+//  - routed_gemm_kernel: the routed experts' gate/up and down, A rows
+//    gathered through each expert's pair list, NVFP4 B tiles dequantised
+//    exactly (E2M1 value times its E4M3 block scale, in fp32, then bf16) into
+//    LDS;
+//  - gemm_kernel: the shared expert's gate/up and down (bf16 B).
+// Epilogues apply the rule: global scale, SwiGLU, bf16 rounding; a
+// memory-bound kernel then forms the weighted combine and the shared add.
 //
-// The routed experts' products use routed_gemm_kernel (below); the dense
-// ones (router, shared expert) use gemm_kernel:
-// Tile: 256 rows x 128 columns, K steps of 32; 4 waves, wave w owns rows
-// [64 w, 64 w + 64) and all 128 columns (2 x 4 MFMA tiles of 32 x 32).
-// Tiles go global -> registers (two K steps ahead) -> LDS (two stages, NVFP4
-// B dequantised on the way), with the 16-byte chunks of each 64-byte LDS row
-// XOR-swizzled so the accesses are spread over the LDS banks.
+// gemm_kernel's tile: 256 rows x 128 columns, K steps of 32; 4 waves, wave w
+// owns rows [64 w, 64 w + 64) and all 128 columns (2 x 4 MFMA tiles of
+// 32 x 32).  Tiles go global -> registers (two K steps ahead) -> LDS (two
+// stages), with the 16-byte chunks of each 64-byte LDS row XOR-swizzled so
+// the accesses are spread over the LDS banks.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -36,7 +36,7 @@ namespace flint {
 namespace {
 
 constexpr int kGThreads = 256;
-constexpr int kBM = 256;  // tile rows (pairs or tokens)
+constexpr int kBM = 256;  // tile rows (tokens)
 constexpr int kBN = 128;  // tile columns (B rows)
 constexpr int kBK = 32;   // K per step (4 chunks of 8 bf16)
 constexpr int kStages = 2;  // LDS stages; register loads run two K steps ahead
@@ -45,7 +45,6 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
 enum GemmMode {
-  kRouter = 0,       // logits[t, c] = bf16(x[t] . R[c])
   kSharedGateUp = 1, // sact[t, n] = bf16(swiglu(x[t] . Wg[n], x[t] . Wu[n]))
   kSharedDown = 2,   // sh[t, h] = bf16(sact[t] . Wd[h])
   kRoutedGateUp = 3, // act[p, n] = bf16(swiglu(a13 x[t(p)] . W13[n], a13 x[t(p)] . W13[I+n]))
@@ -54,11 +53,11 @@ enum GemmMode {
 
 struct GemmArgs {
   const uint16_t *a;     // A source rows (x, sact or act), row length K
-  const uint8_t *b;      // B: bf16 rows, or NVFP4 codes
-  const uint8_t *bs;     // NVFP4 scales (else NULL)
-  const float *alpha;    // NVFP4 global scales [E] (else NULL)
+  const uint8_t *b;      // B: bf16 rows (shared), or NVFP4 codes (routed)
+  const uint8_t *bs;     // NVFP4 scales (routed)
+  const float *alpha;    // NVFP4 global scales [E] (routed)
   uint16_t *c;           // output rows
-  int rows;              // dense modes: number of A rows (tokens)
+  int rows;              // shared expert: number of A rows (tokens)
   int a_rows;            // rows of the A matrix (its extent for the loads)
   int K;                 // reduction length
   int ncols;             // output columns (B rows; for gate/up: act columns)
@@ -77,10 +76,9 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
 
 // LDS position (in 16-byte chunks) of chunk c of tile row r.  The XOR
-// pattern keeps both kinds of access free of bank conflicts: an MFMA operand
-// read (16 lanes a cycle: 16 consecutive rows, one chunk each, a 256-byte
-// bank window) and a dequantised-B store (8 lanes a cycle: 4 rows, chunks
-// 2h + i of lanes (r, h), a 128-byte window).
+// pattern keeps the MFMA operand reads free of bank conflicts (16 lanes a
+// cycle: 16 consecutive rows, one chunk each, a 256-byte bank window); the
+// stores of loaded chunks are 1 KB contiguous per wave.
 __device__ __forceinline__ int swz_x(int r) { return ((r >> 2) & 3) ^ ((r >> 1) & 1); }
 __device__ __forceinline__ int swz(int r, int c) { return r * 4 + (c ^ swz_x(r)); }
 
@@ -101,16 +99,10 @@ __device__ __forceinline__ u32x4_t dequant8(uint32_t codes, float scale) {
                  dequant2<3>(codes, scale)};
 }
 
-template <int MODE>
-struct ModeInfo {
-  static constexpr bool kRouted = MODE == kRoutedGateUp || MODE == kRoutedDown;
-  static constexpr bool kGateUp = MODE == kSharedGateUp || MODE == kRoutedGateUp;
-  static constexpr bool kNvfp4 = kRouted;
-};
-
+// The shared expert's products (MODE kSharedGateUp or kSharedDown).
 template <int MODE>
 __global__ void __launch_bounds__(kGThreads, 2) gemm_kernel(GemmArgs g) {
-  using MI = ModeInfo<MODE>;
+  constexpr bool kGateUp = MODE == kSharedGateUp;
   __shared__ __attribute__((aligned(16))) uint16_t As[kStages][kBM * kBK];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[kStages][kBN * kBK];
   __shared__ int rowidx[kBM];  // A row (token or pair) of each tile row, -1 = none
@@ -118,7 +110,7 @@ __global__ void __launch_bounds__(kGThreads, 2) gemm_kernel(GemmArgs g) {
   __shared__ int tile_info[4];
 
   const int lane = lane_id(), wv = wave_id();
-  const int ntn = MI::kGateUp ? g.ncols / (kBN / 2) : (g.ncols + kBN - 1) / kBN;  // column tiles
+  const int ntn = kGateUp ? g.ncols / (kBN / 2) : (g.ncols + kBN - 1) / kBN;  // column tiles
   // Tile of this block.  Blocks are dealt to the XCDs round-robin; the
   // column tiles of one row tile are given to consecutive blocks of one XCD
   // so its A rows are reused from that XCD's L2.
@@ -126,63 +118,16 @@ __global__ void __launch_bounds__(kGThreads, 2) gemm_kernel(GemmArgs g) {
   const int xcd = blockIdx.x % 8, per = nblk / 8;
   const int b = blockIdx.x < per * 8 ? xcd * per + blockIdx.x / 8 : blockIdx.x;
   const int mt = b / ntn, nt = b % ntn;
-  if constexpr (MI::kRouted) {
-    // row tiles of expert e: ceil(count / 256), rows split evenly over them
-    for (int i = threadIdx.x; i < g.E; i += kGThreads) rowidx[i] = g.counts[i];
-    __syncthreads();
-    if (wv == 0) {
-      int nt4[4], c4[4], tot = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ee = 4 * lane + i;
-        c4[i] = ee < g.E ? rowidx[ee] : 0;
-        nt4[i] = (c4[i] + kBM - 1) / kBM;
-        tot += nt4[i];
-      }
-      int acc = tot;  // exclusive prefix over lanes
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const int t = __shfl_up(acc, o, kWave);
-        if (lane >= o) acc += t;
-      }
-      acc -= tot;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (mt >= acc && mt < acc + nt4[i]) {
-          const int q = mt - acc, c = c4[i], ntile = nt4[i];
-          const int per_t = ((c + ntile - 1) / ntile + 31) / 32 * 32;
-          tile_info[0] = 4 * lane + i;
-          tile_info[1] = q * per_t;
-          tile_info[2] = min(per_t, c - q * per_t);
-        }
-        acc += nt4[i];
-      }
-      if (lane == kWave - 1 && mt >= acc) tile_info[0] = -1;  // beyond the last tile
-    }
-  } else if (threadIdx.x == 0) {
-    tile_info[0] = 0;
-    tile_info[1] = mt * kBM;
-    tile_info[2] = min(kBM, g.rows - mt * kBM);
-  }
-  __syncthreads();
-  const int e = tile_info[0], m0 = tile_info[1], nrows = tile_info[2];
-  if (e < 0 || nrows <= 0) return;
-  const int n0 = nt * (MI::kGateUp ? kBN / 2 : kBN);
+  const int m0 = mt * kBM, nrows = min(kBM, g.rows - m0);
+  if (nrows <= 0) return;
+  const int n0 = nt * (kGateUp ? kBN / 2 : kBN);
 
   // Row indices of the tile; rows past the end repeat the first row (their
   // loads stay in bounds and their results are dropped).
   for (int i = threadIdx.x; i < kBM; i += kGThreads) {
-    const int ii = i < nrows ? i : 0;
-    int src, dst;
-    if constexpr (MI::kRouted) {
-      const int p = g.lists[(size_t)e * g.list_stride + m0 + ii];
-      dst = p;
-      src = MODE == kRoutedGateUp ? p / g.top_k : p;
-    } else {
-      src = dst = m0 + ii;
-    }
+    const int src = m0 + (i < nrows ? i : 0);
     rowidx[i] = src;
-    outrow[i] = i < nrows ? dst : -1;
+    outrow[i] = i < nrows ? src : -1;
   }
   __syncthreads();
 
@@ -190,11 +135,10 @@ __global__ void __launch_bounds__(kGThreads, 2) gemm_kernel(GemmArgs g) {
   const int nk = K / kBK;
   // B row of tile column r
   auto brow = [&](int r) -> int {
-    if constexpr (MI::kGateUp) return r < kBN / 2 ? n0 + r : g.I + n0 + (r - kBN / 2);
+    if constexpr (kGateUp) return r < kBN / 2 ? n0 + r : g.I + n0 + (r - kBN / 2);
     else return n0 + r;
   };
-  const int ncols_b = MI::kGateUp ? 2 * g.I : g.ncols;  // valid B rows
-  const size_t bexp_rows = (size_t)e * ncols_b;          // expert offset in rows (routed)
+  const int ncols_b = kGateUp ? 2 * g.I : g.ncols;  // valid B rows
 
   // ---- loaders.  Each K step moves 256 x 32 A values and 128 x 32 B
   // values (as 16-byte chunks) global -> registers -> LDS.  Thread slot
@@ -223,52 +167,31 @@ __global__ void __launch_bounds__(kGThreads, 2) gemm_kernel(GemmArgs g) {
     const int sl = (u * 4 + wv) * kWave + lane;
     const int r = sl >> 2, c = (sl & 3) ^ swz_x(r);
     const int br = brow(r) < ncols_b ? brow(r) : 0;  // columns past the end: dropped
-    b_off[u] = MI::kNvfp4 ? 0u : (uint32_t)(((size_t)br * K + c * 8) * 2);
+    b_off[u] = (uint32_t)(((size_t)br * K + c * 8) * 2);
     b_slot[u] = sl;
   }
-  // NVFP4 B: thread t dequantises 16 elements of row t / 2 (half t % 2)
-  const int br_t = threadIdx.x >> 1, bh_t = threadIdx.x & 1;
-  const uint32_t bc_off = (uint32_t)(brow(br_t) * (K / 2) + bh_t * 8);
-  const uint32_t bs_off = (uint32_t)(brow(br_t) * (K / 16) + bh_t);
   const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(g.a, (size_t)g.a_rows * K * 2);
-  const __amdgpu_buffer_rsrc_t rs_b =
-      MI::kNvfp4 ? make_rsrc(g.b + bexp_rows * (K / 2), (size_t)ncols_b * (K / 2))
-                 : make_rsrc(g.b, (size_t)ncols_b * K * 2);
-  const __amdgpu_buffer_rsrc_t rs_s =
-      make_rsrc(MI::kNvfp4 ? g.bs + bexp_rows * (K / 16) : g.b, MI::kNvfp4 ? (size_t)ncols_b * (K / 16) : 0);
+  const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(g.b, (size_t)ncols_b * K * 2);
 
   struct Regs {
     u32x4_t a[4];
-    u32x4_t b[2];     // bf16 B
-    uint2 codes;      // NVFP4 B
-    uint32_t scale;
+    u32x4_t b[2];
   };
   auto load = [&](Regs &R, int kb) {
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       R.a[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_a, a_off[u], kb * kBK * 2, 0));
-    if constexpr (MI::kNvfp4) {
-      R.codes = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs_b, bc_off, kb * (kBK / 2), 0));
-      R.scale = __builtin_amdgcn_raw_buffer_load_b8(rs_s, bs_off, kb * 2, 0);
-    } else {
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-        R.b[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_b, b_off[u], kb * kBK * 2, 0));
-    }
+    for (int u = 0; u < 2; ++u)
+      R.b[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_b, b_off[u], kb * kBK * 2, 0));
   };
   auto store = [&](int stage, const Regs &R) {
     u32x4_t *as = reinterpret_cast<u32x4_t *>(&As[stage][0]);
     u32x4_t *bs = reinterpret_cast<u32x4_t *>(&Bs[stage][0]);
 #pragma unroll
     for (int u = 0; u < 4; ++u) as[a_slot[u]] = R.a[u];
-    if constexpr (MI::kNvfp4) {
-      const float sc = e4m3_to_f32(R.scale);
-      bs[swz(br_t, 2 * bh_t)] = dequant8(R.codes.x, sc);
-      bs[swz(br_t, 2 * bh_t + 1)] = dequant8(R.codes.y, sc);
-    } else {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) bs[b_slot[u]] = R.b[u];
-    }
+    for (int u = 0; u < 2; ++u) bs[b_slot[u]] = R.b[u];
   };
 
   f32x16_t acc[2][4];
@@ -337,7 +260,6 @@ __global__ void __launch_bounds__(kGThreads, 2) gemm_kernel(GemmArgs g) {
 
   // ---- epilogue: acc[m][n][r] is C[row, col], row = 64 wv + 32 m + 8 (r / 4)
   // + 4 (lane / 32) + r % 4, col = 32 n + lane % 32.
-  const float alpha = MI::kNvfp4 ? g.alpha[e] : 1.0f;
   const int cl = lane & 31;
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
@@ -347,26 +269,11 @@ __global__ void __launch_bounds__(kGThreads, 2) gemm_kernel(GemmArgs g) {
       const int row = 64 * wv + 32 * m + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
       if (row >= nrows) continue;
       const int orow = outrow[row];
-      if constexpr (MI::kGateUp) {
+      if constexpr (kGateUp) {
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
-          float gs = acc[m][n][r], us = acc[m][n + 2][r];
-          if constexpr (MI::kNvfp4) {
-            gs = gs * alpha;
-            us = us * alpha;
-          }
           const int col = n0 + 32 * n + cl;
-          g.c[(size_t)orow * g.ldc + col] = (uint16_t)f32_to_bf16(swiglu(gs, us));
-        }
-      } else if constexpr (MODE == kRoutedDown) {
-#pragma unroll
-        for (int n = 0; n < 4; ++n)
-          g.c[(size_t)orow * g.ldc + n0 + 32 * n + cl] = (uint16_t)f32_to_bf16(acc[m][n][r] * alpha);
-      } else if constexpr (MODE == kRouter) {
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          const int col = n0 + 32 * n + cl;
-          if (col < g.ncols) g.c[(size_t)orow * g.ldc + col] = (uint16_t)f32_to_bf16(acc[m][n][r]);
+          g.c[(size_t)orow * g.ldc + col] = (uint16_t)f32_to_bf16(swiglu(acc[m][n][r], acc[m][n + 2][r]));
         }
       } else {  // kSharedDown
 #pragma unroll
