@@ -29,6 +29,7 @@
 #include "common.hpp"
 #include "internal.hpp"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace flint {
@@ -308,6 +309,7 @@ constexpr int kRBM = 256;   // tile rows
 constexpr int kRBN = 256;   // tile columns (B rows)
 constexpr int kRBK = 64;    // K per stage
 constexpr int kRStages = 3; // LDS buffers of dequantised B
+constexpr int kMaxTiles = 64; // tiles per block (the grid is sized for it)
 
 // 16-byte chunk c (0..7, k = 8c .. 8c + 7 of the stage) of tile column r.
 // Conflict-free for the MFMA reads (16 lanes: 16 consecutive columns, one
@@ -322,30 +324,31 @@ __global__ void __launch_bounds__(kGThreads, 1) routed_gemm_kernel(GemmArgs g) {
   constexpr bool kGU = MODE == kRoutedGateUp;
   constexpr int BN = kRBN, NN = BN / 32;  // tile columns, MFMA column tiles
   __shared__ u32x4_t Bs[kRStages][BN * 8];
-  __shared__ int rowidx[kRBM];  // A row (token or pair) of each tile row
-  __shared__ int outrow[kRBM];  // output row of each tile row, -1 = none
-  __shared__ int tile_info[4];
+  __shared__ int rows_s[2][kRBM];      // A row (token or pair) of each tile row, by tile parity
+  __shared__ int outs_s[2][kRBM];      // output row of each tile row, -1 = none
+  __shared__ int4 tiles_s[kMaxTiles];  // (expert, first pair, rows, column tile)
+  __shared__ int ntiles_s;
 
   const int lane = lane_id(), wv = wave_id();
   const int colw = kGU ? BN / 2 : BN;  // output columns per tile
   const int ntn = (g.ncols + colw - 1) / colw;
 
-  // Tile of this block.  Expert e has ceil(count_e / 256) row tiles, all
+  // This block's tiles.  Expert e has ceil(count_e / 256) row tiles, all
   // full but its last.  Row tiles are ordered by cost: every full tile, then
   // the partial ones of more than 128 rows (two slices on some wave: a full
   // tile's time), then those of at most 128 rows (half that), each class in
-  // expert order.  Row tile rt goes to XCD rt % 8 (blocks are dealt to the
-  // XCDs round-robin), where its column tiles run on consecutive blocks and
-  // share that XCD's L2; each XCD takes its tiles costliest first, so the
-  // cheap ones fill the end of the launch.  Blocks past the work exit.
-  for (int i = threadIdx.x; i < g.E; i += kGThreads) rowidx[i] = g.counts[i];
+  // expert order.  Row tile rt belongs to XCD rt % 8 (blocks are dealt to
+  // the XCDs round-robin); an XCD's tiles, row tile by row tile with its
+  // column tiles consecutive (they share the XCD's L2), are dealt to its
+  // blocks costliest first.
+  for (int i = threadIdx.x; i < g.E; i += kGThreads) rows_s[0][i] = g.counts[i];
   __syncthreads();
   if (wv == 0) {
     int c4[4], nf[4], nl[4], ns[4], tf = 0, tl = 0, ts = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ee = 4 * lane + i;
-      c4[i] = ee < g.E ? rowidx[ee] : 0;
+      c4[i] = ee < g.E ? rows_s[0][ee] : 0;
       const int rem = c4[i] % kRBM;
       nf[i] = c4[i] / kRBM;
       nl[i] = rem > kRBM / 2;
@@ -366,40 +369,57 @@ __global__ void __launch_bounds__(kGThreads, 1) routed_gemm_kernel(GemmArgs g) {
     }
     const int TF = __shfl(pf, kWave - 1, kWave), TL = __shfl(pl, kWave - 1, kWave),
               TS = __shfl(ps, kWave - 1, kWave);
-    const int i8 = blockIdx.x / 8;
-    const int rt = (i8 / ntn) * 8 + blockIdx.x % 8;  // row tile
-    // class of rt and its index within the class
-    const int cls = rt < TF ? 0 : (rt < TF + TL ? 1 : 2);
-    const int j = cls == 0 ? rt : (cls == 1 ? rt - TF : rt - TF - TL);
-    int acc = cls == 0 ? pf - tf : (cls == 1 ? pl - tl : ps - ts);
-    const bool ok = rt < TF + TL + TS;
+    const int x = blockIdx.x % 8, S = gridDim.x / 8, T = TF + TL + TS;
+    const int L = (T > x ? (T - x + 7) / 8 : 0) * ntn;  // this XCD's tiles
+    // round r of the deal gives block j the XCD's tile r S + j (r even) or
+    // r S + S - 1 - j (r odd), which evens out the cost-ordered list
+    const int jb = blockIdx.x / 8;
+    int n = 0;
+    for (int r = 0; r * S < L && n < kMaxTiles; ++r) {
+      const int i = r * S + ((r & 1) ? S - 1 - jb : jb);
+      if (i >= L) continue;
+      const int rt = x + 8 * (i / ntn);
+      const int cls = rt < TF ? 0 : (rt < TF + TL ? 1 : 2);
+      const int j = cls == 0 ? rt : (cls == 1 ? rt - TF : rt - TF - TL);
+      int acc = cls == 0 ? pf - tf : (cls == 1 ? pl - tl : ps - ts);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int n = cls == 0 ? nf[i] : (cls == 1 ? nl[i] : ns[i]);
-      if (ok && j >= acc && j < acc + n) {
-        const int q = cls == 0 ? j - acc : nf[i];
-        tile_info[0] = 4 * lane + i;
-        tile_info[1] = q * kRBM;
-        tile_info[2] = min(kRBM, c4[i] - q * kRBM);
-        tile_info[3] = i8 % ntn;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int cnt = cls == 0 ? nf[q4] : (cls == 1 ? nl[q4] : ns[q4]);
+        if (j >= acc && j < acc + cnt) {
+          const int q = cls == 0 ? j - acc : nf[q4];
+          tiles_s[n] = make_int4(4 * lane + q4, q * kRBM, min(kRBM, c4[q4] - q * kRBM), i % ntn);
+        }
+        acc += cnt;
       }
-      acc += n;
+      ++n;
     }
-    if (!ok && lane == 0) tile_info[0] = -1;
+    if (lane == 0) ntiles_s = n;
   }
   __syncthreads();
-  const int e = tile_info[0];
-  if (e < 0) return;
-  const int m0 = tile_info[1], nrows = tile_info[2], nt = tile_info[3];
-  {
-    // rows past the end repeat the first (loaded by no live slice)
-    const int i = threadIdx.x;
-    const int p = g.lists[(size_t)e * g.list_stride + m0 + (i < nrows ? i : 0)];
-    rowidx[i] = kGU ? p / g.top_k : p;
-    outrow[i] = i < nrows ? p : -1;
-  }
+  const int ntiles = ntiles_s;
+  if (ntiles == 0) return;
+  // Row lists: this thread's entry (tile row threadIdx.x) of tile k; rows
+  // past the tile's end repeat its first (loaded by no live slice).
+  auto fetch_row = [&](int k) -> int {
+    const int4 t = tiles_s[k];
+    return g.lists[(size_t)t.x * g.list_stride + t.y + ((int)threadIdx.x < t.z ? threadIdx.x : 0)];
+  };
+  auto store_row = [&](int slot, int k, int p) {
+    rows_s[slot][threadIdx.x] = kGU ? p / g.top_k : p;
+    outs_s[slot][threadIdx.x] = (int)threadIdx.x < tiles_s[k].z ? p : -1;
+  };
+  store_row(0, 0, fetch_row(0));  // (rows_s[0] held the counts: read above)
   __syncthreads();
 
+  for (int k = 0; k < ntiles; ++k) {
+  // the next tile's row list, in flight during this one (past the last
+  // tile: a repeat of it, unused)
+  const int pnext = fetch_row(min(k + 1, ntiles - 1));
+  const int e = __builtin_amdgcn_readfirstlane(tiles_s[k].x);
+  const int nrows = __builtin_amdgcn_readfirstlane(tiles_s[k].z);
+  const int nt = __builtin_amdgcn_readfirstlane(tiles_s[k].w);
+  const int *rowidx = rows_s[k & 1];
+  const int *outrow = outs_s[k & 1];
   const int K = g.K, nk = K / kRBK;
   const int n0 = nt * colw;
   // B row of this thread's tile column (gate/up: columns 0..127 gate rows
@@ -546,6 +566,9 @@ __global__ void __launch_bounds__(kGThreads, 1) routed_gemm_kernel(GemmArgs g) {
     }
     if (s < nk) stage(IC<0>{}, s);
     if (s + 1 < nk) stage(IC<1>{}, s + 1);
+    // the next tile's rows into the other slot (read after the barrier that
+    // starts the next tile)
+    store_row((k + 1) & 1, min(k + 1, ntiles - 1), pnext);
 
     // acc[m][n][r]: row 32 (wv + 4 m) + lane % 32, column 32 n + 8 (r / 4) +
     // 4 (lane / 32) + r % 4 of the tile.
@@ -574,6 +597,8 @@ __global__ void __launch_bounds__(kGThreads, 1) routed_gemm_kernel(GemmArgs g) {
   if (nm == 2) run(IC<2>{});
   else if (nm == 1) run(IC<1>{});
   else run(IC<0>{});
+  __syncthreads();
+  }
 }
 
 // Router logits of the grouped path: logits[t, c] = bf16(fp32 x[t] . R[c]).
@@ -783,14 +808,16 @@ hipError_t launch_gemm(const GemmArgs &g, int row_tiles, int col_tiles, hipStrea
   return hipGetLastError();
 }
 
-// Grid: every XCD gets ceil(row_tiles / 8) row tiles' worth of blocks
-// (row_tiles: an upper bound on the actual count, known on the device).
+// One block per CU (32 per XCD), more if an XCD's tiles would exceed
+// kMaxTiles per block (row_tiles bounds the actual count, known on the
+// device).
 template <int MODE>
 hipError_t launch_routed(const GemmArgs &g, int row_tiles, hipStream_t st) {
   const int colw = MODE == kRoutedGateUp ? kRBN / 2 : kRBN;
   const int col_tiles = (g.ncols + colw - 1) / colw;
-  const int nblk = (row_tiles + 7) / 8 * 8 * col_tiles;
-  if (nblk <= 0) return hipSuccess;
+  const long per_xcd = (long)(row_tiles + 7) / 8 * col_tiles;
+  if (per_xcd <= 0) return hipSuccess;
+  const int nblk = 8 * (int)std::max<long>(32, (per_xcd + kMaxTiles - 1) / kMaxTiles);
   hipLaunchKernelGGL((routed_gemm_kernel<MODE>), dim3(nblk), dim3(kGThreads), 0, st, g);
   return hipGetLastError();
 }
