@@ -30,6 +30,7 @@
 #include "internal.hpp"
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 namespace flint {
@@ -822,6 +823,36 @@ hipError_t launch_routed(const GemmArgs &g, int row_tiles, hipStream_t st) {
   return hipGetLastError();
 }
 
+
+
+// The shared expert's two GEMMs depend on x only; without stage events they
+// run on a second stream of the device (created on first use, kept for the
+// process, default priority) so their blocks fill the CUs the routed GEMMs
+// leave idle at their ends.  The caller's stream forks to it after the
+// router (an event) and joins it before the combine (another event).
+// Enqueueing a call's fork and join is serialised per device by a mutex, so
+// calls from several host threads cannot interleave their event records.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+SideStream g_side[kMaxDevices];
+std::mutex g_side_mu[kMaxDevices];
+
+hipError_t side_stream(int dev, SideStream **out) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  SideStream &sd = g_side[dev];
+  if (!sd.s) {
+    hipError_t e;
+    if ((e = hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&sd.join, hipEventDisableTiming)) != hipSuccess) return e;
+  }
+  *out = &sd;
+  return hipSuccess;
+}
+
 }  // namespace
 
 bool grouped_shape_supported(int H, int I, int SI) {
@@ -849,8 +880,35 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
   if ((err = mark(1)) != hipSuccess) return err;
   hipLaunchKernelGGL(plan_lists_kernel, dim3(E), dim3(256), 0, st, a.ids, P, a.lists, M, a.counts);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  // 3. shared gate/up
+  // 3. shared gate/up (and 6. shared down): on the side stream unless
+  // stage events are asked for
   if ((err = mark(2)) != hipSuccess) return err;
+  const bool side = a.sgu && !a.events;
+  hipStream_t sst = st;
+  std::unique_lock<std::mutex> side_lock;
+  SideStream *sd = nullptr;
+  if (side) {
+    int dev = 0;
+    if ((err = hipGetDevice(&dev)) != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    side_lock = std::unique_lock<std::mutex>(g_side_mu[dev]);
+    if ((err = side_stream(dev, &sd)) != hipSuccess) return err;
+    if ((err = hipEventRecord(sd->fork, st)) != hipSuccess) return err;
+    if ((err = hipStreamWaitEvent(sd->s, sd->fork, 0)) != hipSuccess) return err;
+    sst = sd->s;
+  }
+  auto shared_down = [&]() -> hipError_t {
+    GemmArgs sdn{};
+    sdn.a = a.sact;
+    sdn.b = reinterpret_cast<const uint8_t *>(a.sdown);
+    sdn.c = a.sh;
+    sdn.rows = M;
+    sdn.a_rows = M;
+    sdn.K = SI;
+    sdn.ncols = H;
+    sdn.ldc = H;
+    return launch_gemm<kSharedDown>(sdn, (M + kBM - 1) / kBM, H / kBN, sst);
+  };
   if (a.sgu) {
     GemmArgs s{};
     s.a = a.x;
@@ -862,8 +920,12 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
     s.ncols = SI;
     s.ldc = SI;
     s.I = SI;
-    if ((err = launch_gemm<kSharedGateUp>(s, (M + kBM - 1) / kBM, SI / (kBN / 2), st)) != hipSuccess)
+    if ((err = launch_gemm<kSharedGateUp>(s, (M + kBM - 1) / kBM, SI / (kBN / 2), sst)) != hipSuccess)
       return err;
+    if (side) {
+      if ((err = shared_down()) != hipSuccess) return err;
+      if ((err = hipEventRecord(sd->join, sst)) != hipSuccess) return err;
+    }
   }
   // 4. routed gate/up: row tiles bounded by sum_e ceil(count_e / 256)
   if ((err = mark(3)) != hipSuccess) return err;
@@ -907,19 +969,12 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
     dn.E = E;
     if ((err = launch_routed<kRoutedDown>(dn, max_row_tiles, st)) != hipSuccess) return err;
   }
-  // 6. shared down -> sh
+  // 6. shared down -> sh (already queued on the side stream: join it)
   if ((err = mark(5)) != hipSuccess) return err;
-  if (a.sgu) {
-    GemmArgs sd{};
-    sd.a = a.sact;
-    sd.b = reinterpret_cast<const uint8_t *>(a.sdown);
-    sd.c = a.sh;
-    sd.rows = M;
-    sd.a_rows = M;
-    sd.K = SI;
-    sd.ncols = H;
-    sd.ldc = H;
-    if ((err = launch_gemm<kSharedDown>(sd, (M + kBM - 1) / kBM, H / kBN, st)) != hipSuccess) return err;
+  if (side) {
+    if ((err = hipStreamWaitEvent(st, sd->join, 0)) != hipSuccess) return err;
+  } else if (a.sgu) {
+    if ((err = shared_down()) != hipSuccess) return err;
   }
   // 7. combine + shared add
   if ((err = mark(6)) != hipSuccess) return err;
