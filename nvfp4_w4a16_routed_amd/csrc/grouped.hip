@@ -413,192 +413,192 @@ __global__ void __launch_bounds__(kGThreads, 1) routed_gemm_kernel(GemmArgs g) {
   __syncthreads();
 
   for (int k = 0; k < ntiles; ++k) {
-  // the next tile's row list, in flight during this one (past the last
-  // tile: a repeat of it, unused)
-  const int pnext = fetch_row(min(k + 1, ntiles - 1));
-  const int e = __builtin_amdgcn_readfirstlane(tiles_s[k].x);
-  const int nrows = __builtin_amdgcn_readfirstlane(tiles_s[k].z);
-  const int nt = __builtin_amdgcn_readfirstlane(tiles_s[k].w);
-  const int *rowidx = rows_s[k & 1];
-  const int *outrow = outs_s[k & 1];
-  const int K = g.K, nk = K / kRBK;
-  const int n0 = nt * colw;
-  // B row of this thread's tile column (gate/up: columns 0..127 gate rows
-  // n0 + c, 128..255 the matching up rows I + n0 + c); past the end: row 0.
-  const int tc = threadIdx.x;
-  int brow;
-  if constexpr (kGU) {
-    const int c = n0 + (tc & (BN / 2 - 1));
-    brow = c < g.ncols ? (tc < BN / 2 ? c : g.I + c) : 0;
-  } else {
-    const int c = n0 + tc;
-    brow = c < g.ncols ? c : 0;
-  }
-  const int ncols_b = kGU ? 2 * g.I : g.ncols;
-  const size_t bexp = (size_t)e * ncols_b;
-  const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(g.a, (size_t)g.a_rows * K * 2);
-  const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(g.b + bexp * (K / 2), (size_t)ncols_b * (K / 2));
-  const __amdgpu_buffer_rsrc_t rs_s = make_rsrc(g.bs + bexp * (K / 16), (size_t)ncols_b * (K / 16));
-  const uint32_t bc_off = (uint32_t)brow * (K / 2), bs_off = (uint32_t)brow * (K / 16);
+    // the next tile's row list, in flight during this one (past the last
+    // tile: a repeat of it, unused)
+    const int pnext = fetch_row(min(k + 1, ntiles - 1));
+    const int e = __builtin_amdgcn_readfirstlane(tiles_s[k].x);
+    const int nrows = __builtin_amdgcn_readfirstlane(tiles_s[k].z);
+    const int nt = __builtin_amdgcn_readfirstlane(tiles_s[k].w);
+    const int *rowidx = rows_s[k & 1];
+    const int *outrow = outs_s[k & 1];
+    const int K = g.K, nk = K / kRBK;
+    const int n0 = nt * colw;
+    // B row of this thread's tile column (gate/up: columns 0..127 gate rows
+    // n0 + c, 128..255 the matching up rows I + n0 + c); past the end: row 0.
+    const int tc = threadIdx.x;
+    int brow;
+    if constexpr (kGU) {
+      const int c = n0 + (tc & (BN / 2 - 1));
+      brow = c < g.ncols ? (tc < BN / 2 ? c : g.I + c) : 0;
+    } else {
+      const int c = n0 + tc;
+      brow = c < g.ncols ? c : 0;
+    }
+    const int ncols_b = kGU ? 2 * g.I : g.ncols;
+    const size_t bexp = (size_t)e * ncols_b;
+    const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(g.a, (size_t)g.a_rows * K * 2);
+    const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(g.b + bexp * (K / 2), (size_t)ncols_b * (K / 2));
+    const __amdgpu_buffer_rsrc_t rs_s = make_rsrc(g.bs + bexp * (K / 16), (size_t)ncols_b * (K / 16));
+    const uint32_t bc_off = (uint32_t)brow * (K / 2), bs_off = (uint32_t)brow * (K / 16);
 
-  // live 32-row slices of this wave: w (m = 0) and w + 4 (m = 1)
-  const int nh = (nrows + 31) / 32;
-  const int nm = (nh > wv) + (nh > wv + 4);
-  const int h = lane >> 5;
-  uint32_t a_off[2];
+    // live 32-row slices of this wave: w (m = 0) and w + 4 (m = 1)
+    const int nh = (nrows + 31) / 32;
+    const int nm = (nh > wv) + (nh > wv + 4);
+    const int h = lane >> 5;
+    uint32_t a_off[2];
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
-    a_off[m] = (uint32_t)rowidx[32 * (wv + 4 * m) + (lane & 31)] * (uint32_t)(K * 2) + h * 16;
+    for (int m = 0; m < 2; ++m)
+      a_off[m] = (uint32_t)rowidx[32 * (wv + 4 * m) + (lane & 31)] * (uint32_t)(K * 2) + h * 16;
 
-  struct Codes {
-    u32x4_t c[2];  // 64 E2M1 codes: k = 32 i + 0..31
-    uint32_t s;    // 4 E4M3 scales, one per 16 k
-  };
-  auto load_codes = [&](Codes &C, int s) {
-    C.c[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_b, bc_off, s * 32, 0));
-    C.c[1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_b, bc_off, s * 32 + 16, 0));
-    C.s = __builtin_amdgcn_raw_buffer_load_b32(rs_s, bs_off, s * 4, 0);
-  };
-  // Chunks 2 q and 2 q + 1 (k = 16 q .. 16 q + 15, scale byte q) of this
-  // thread's column into an LDS buffer.
-  auto dequant_pair = [&](u32x4_t *buf, const Codes &C, auto q_c) {
-    constexpr int q = decltype(q_c)::value;
-    const float sc = __builtin_amdgcn_cvt_f32_fp8((int)C.s, q);
-    const u32x4_t &cw = C.c[q >> 1];
-    buf[rswz(tc, 2 * q)] = dequant8(cw[2 * (q & 1)], sc);
-    buf[rswz(tc, 2 * q + 1)] = dequant8(cw[2 * (q & 1) + 1], sc);
-  };
-  auto dequant_store = [&](u32x4_t *buf, const Codes &C) {
-    dequant_pair(buf, C, IC<0>{});
-    dequant_pair(buf, C, IC<1>{});
-    dequant_pair(buf, C, IC<2>{});
-    dequant_pair(buf, C, IC<3>{});
-  };
-  const float alpha = g.alpha[e];
-
-  auto run = [&](auto nm_c) {
-    constexpr int NM = decltype(nm_c)::value;
-    constexpr int NA = NM > 0 ? NM : 1;
-    f32x16_t acc[NA][NN];
-#pragma unroll
-    for (int m = 0; m < NA; ++m)
-#pragma unroll
-      for (int n = 0; n < NN; ++n)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.0f;
-    u32x4_t A[3][NA][4];
-    Codes C[3];
-    auto load_a_m = [&](u32x4_t (&dst)[4], int m, int s) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        dst[q] = __builtin_bit_cast(
-            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_a, a_off[m], s * (kRBK * 2) + q * 32, 0));
+    struct Codes {
+      u32x4_t c[2];  // 64 E2M1 codes: k = 32 i + 0..31
+      uint32_t s;    // 4 E4M3 scales, one per 16 k
     };
-    auto load_a = [&](u32x4_t (&dst)[NA][4], int s) {
+    auto load_codes = [&](Codes &C, int s) {
+      C.c[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_b, bc_off, s * 32, 0));
+      C.c[1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_b, bc_off, s * 32 + 16, 0));
+      C.s = __builtin_amdgcn_raw_buffer_load_b32(rs_s, bs_off, s * 4, 0);
+    };
+    // Chunks 2 q and 2 q + 1 (k = 16 q .. 16 q + 15, scale byte q) of this
+    // thread's column into an LDS buffer.
+    auto dequant_pair = [&](u32x4_t *buf, const Codes &C, auto q_c) {
+      constexpr int q = decltype(q_c)::value;
+      const float sc = __builtin_amdgcn_cvt_f32_fp8((int)C.s, q);
+      const u32x4_t &cw = C.c[q >> 1];
+      buf[rswz(tc, 2 * q)] = dequant8(cw[2 * (q & 1)], sc);
+      buf[rswz(tc, 2 * q + 1)] = dequant8(cw[2 * (q & 1) + 1], sc);
+    };
+    auto dequant_store = [&](u32x4_t *buf, const Codes &C) {
+      dequant_pair(buf, C, IC<0>{});
+      dequant_pair(buf, C, IC<1>{});
+      dequant_pair(buf, C, IC<2>{});
+      dequant_pair(buf, C, IC<3>{});
+    };
+    const float alpha = g.alpha[e];
+
+    auto run = [&](auto nm_c) {
+      constexpr int NM = decltype(nm_c)::value;
+      constexpr int NA = NM > 0 ? NM : 1;
+      f32x16_t acc[NA][NN];
 #pragma unroll
-      for (int m = 0; m < NM; ++m)
+      for (int m = 0; m < NA; ++m)
+#pragma unroll
+        for (int n = 0; n < NN; ++n)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.0f;
+      u32x4_t A[3][NA][4];
+      Codes C[3];
+      auto load_a_m = [&](u32x4_t (&dst)[4], int m, int s) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          dst[m][q] = __builtin_bit_cast(
+          dst[q] = __builtin_bit_cast(
               u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_a, a_off[m], s * (kRBK * 2) + q * 32, 0));
-    };
-    // Stage s (J = s % 3) computes from LDS buffer J and registers A[J]; the
-    // B tile of s + 1 is already in buffer J + 1 and s + 2's is dequantised
-    // into buffer J + 2 during the stage, so the operand reads run ahead
-    // across the stage's barrier (which only orders the dequant stores of
-    // the next stage after this stage's reads of the buffer they reuse).
-    // Requests: codes of s + 4 and A of s + 2, in the order they are
-    // consumed, so each wait covers only what it needs.  Sub-step q reads
-    // the B operands of the next sub-step (for q = 3: sub-step 0 of s + 1),
-    // runs the MFMAs of q and dequantises a quarter of the codes of s + 2;
-    // scheduling barriers keep each sub-step's work together.  Past the last
-    // stage the loads repeat it and the stores fill a buffer never read.
-    u32x4_t bf[2][NN];
-    auto read_b = [&](u32x4_t (&dst)[NN], const u32x4_t *buf, int sub) {
-      if constexpr (NM > 0) {
-#pragma unroll
-        for (int n = 0; n < NN; ++n) dst[n] = buf[rswz(32 * n + (lane & 31), 2 * sub + h)];
-      }
-    };
-    auto stage = [&](auto j_c, int s) {
-      constexpr int J = decltype(j_c)::value, J1 = (J + 1) % 3, J2 = (J + 2) % 3;
-      auto sub_step = [&](auto q_c) {
-        constexpr int q = decltype(q_c)::value;
-        // the stage's requests, spread over the first sub-steps
-        if constexpr (q == 0) load_codes(C[J1], min(s + 4, nk - 1));
-        if constexpr (q == 1 && NM > 0) load_a_m(A[J2][0], 0, min(s + 2, nk - 1));
-        if constexpr (q == 2 && NM > 1) load_a_m(A[J2][1], 1, min(s + 2, nk - 1));
-        if constexpr (q < 3) read_b(bf[(q + 1) & 1], Bs[J], q + 1);
-        else read_b(bf[0], Bs[J1], 0);
+      };
+      auto load_a = [&](u32x4_t (&dst)[NA][4], int s) {
 #pragma unroll
         for (int m = 0; m < NM; ++m)
 #pragma unroll
-          for (int n = 0; n < NN; ++n)
-            acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, bf[q & 1][n]),
-                                                                __builtin_bit_cast(bf16x8_t, A[J][m][q]),
-                                                                acc[m][n], 0, 0, 0);
-        dequant_pair(Bs[J2], C[J2], q_c);
-        __builtin_amdgcn_sched_barrier(0);
+          for (int q = 0; q < 4; ++q)
+            dst[m][q] = __builtin_bit_cast(
+                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_a, a_off[m], s * (kRBK * 2) + q * 32, 0));
       };
-      sub_step(IC<0>{});
-      sub_step(IC<1>{});
-      sub_step(IC<2>{});
-      sub_step(IC<3>{});
-      __syncthreads();
-    };
-
-    // prologue: B tiles 0 and 1 in LDS, codes of 2 and 3 and A of 0 and 1
-    // requested, B operands of stage 0's first sub-step read
-    load_codes(C[0], 0);
-    load_codes(C[1], min(1, nk - 1));
-    load_codes(C[2], min(2, nk - 1));
-    load_a(A[0], 0);
-    load_a(A[1], min(1, nk - 1));
-    dequant_store(Bs[0], C[0]);
-    dequant_store(Bs[1], C[1]);
-    load_codes(C[0], min(3, nk - 1));
-    __syncthreads();
-    read_b(bf[0], Bs[0], 0);
-    int s = 0;
-    for (; s + 3 <= nk; s += 3) {
-      stage(IC<0>{}, s);
-      stage(IC<1>{}, s + 1);
-      stage(IC<2>{}, s + 2);
-    }
-    if (s < nk) stage(IC<0>{}, s);
-    if (s + 1 < nk) stage(IC<1>{}, s + 1);
-    // the next tile's rows into the other slot (read after the barrier that
-    // starts the next tile)
-    store_row((k + 1) & 1, min(k + 1, ntiles - 1), pnext);
-
-    // acc[m][n][r]: row 32 (wv + 4 m) + lane % 32, column 32 n + 8 (r / 4) +
-    // 4 (lane / 32) + r % 4 of the tile.
+      // Stage s (J = s % 3) computes from LDS buffer J and registers A[J]; the
+      // B tile of s + 1 is already in buffer J + 1 and s + 2's is dequantised
+      // into buffer J + 2 during the stage, so the operand reads run ahead
+      // across the stage's barrier (which only orders the dequant stores of
+      // the next stage after this stage's reads of the buffer they reuse).
+      // Requests: codes of s + 4 and A of s + 2, in the order they are
+      // consumed, so each wait covers only what it needs.  Sub-step q reads
+      // the B operands of the next sub-step (for q = 3: sub-step 0 of s + 1),
+      // runs the MFMAs of q and dequantises a quarter of the codes of s + 2;
+      // scheduling barriers keep each sub-step's work together.  Past the last
+      // stage the loads repeat it and the stores fill a buffer never read.
+      u32x4_t bf[2][NN];
+      auto read_b = [&](u32x4_t (&dst)[NN], const u32x4_t *buf, int sub) {
+        if constexpr (NM > 0) {
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      const int orow = outrow[32 * (wv + 4 * m) + (lane & 31)];
-      if (orow < 0) continue;
-      uint16_t *crow = g.c + (size_t)orow * g.ldc;
-#pragma unroll
-      for (int n = 0; n < (kGU ? NN / 2 : NN); ++n)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int col = n0 + 32 * n + 8 * gq + 4 * h;
-          if (col >= g.ncols) continue;
-          float o[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if constexpr (kGU)
-              o[i] = swiglu(acc[m][n][4 * gq + i] * alpha, acc[m][n + NN / 2][4 * gq + i] * alpha);
-            else o[i] = acc[m][n][4 * gq + i] * alpha;
-          }
-          *reinterpret_cast<uint2 *>(crow + col) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+          for (int n = 0; n < NN; ++n) dst[n] = buf[rswz(32 * n + (lane & 31), 2 * sub + h)];
         }
-    }
-  };
-  if (nm == 2) run(IC<2>{});
-  else if (nm == 1) run(IC<1>{});
-  else run(IC<0>{});
-  __syncthreads();
+      };
+      auto stage = [&](auto j_c, int s) {
+        constexpr int J = decltype(j_c)::value, J1 = (J + 1) % 3, J2 = (J + 2) % 3;
+        auto sub_step = [&](auto q_c) {
+          constexpr int q = decltype(q_c)::value;
+          // the stage's requests, spread over the first sub-steps
+          if constexpr (q == 0) load_codes(C[J1], min(s + 4, nk - 1));
+          if constexpr (q == 1 && NM > 0) load_a_m(A[J2][0], 0, min(s + 2, nk - 1));
+          if constexpr (q == 2 && NM > 1) load_a_m(A[J2][1], 1, min(s + 2, nk - 1));
+          if constexpr (q < 3) read_b(bf[(q + 1) & 1], Bs[J], q + 1);
+          else read_b(bf[0], Bs[J1], 0);
+#pragma unroll
+          for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int n = 0; n < NN; ++n)
+              acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, bf[q & 1][n]),
+                                                                  __builtin_bit_cast(bf16x8_t, A[J][m][q]),
+                                                                  acc[m][n], 0, 0, 0);
+          dequant_pair(Bs[J2], C[J2], q_c);
+          __builtin_amdgcn_sched_barrier(0);
+        };
+        sub_step(IC<0>{});
+        sub_step(IC<1>{});
+        sub_step(IC<2>{});
+        sub_step(IC<3>{});
+        __syncthreads();
+      };
+
+      // prologue: B tiles 0 and 1 in LDS, codes of 2 and 3 and A of 0 and 1
+      // requested, B operands of stage 0's first sub-step read
+      load_codes(C[0], 0);
+      load_codes(C[1], min(1, nk - 1));
+      load_codes(C[2], min(2, nk - 1));
+      load_a(A[0], 0);
+      load_a(A[1], min(1, nk - 1));
+      dequant_store(Bs[0], C[0]);
+      dequant_store(Bs[1], C[1]);
+      load_codes(C[0], min(3, nk - 1));
+      __syncthreads();
+      read_b(bf[0], Bs[0], 0);
+      int s = 0;
+      for (; s + 3 <= nk; s += 3) {
+        stage(IC<0>{}, s);
+        stage(IC<1>{}, s + 1);
+        stage(IC<2>{}, s + 2);
+      }
+      if (s < nk) stage(IC<0>{}, s);
+      if (s + 1 < nk) stage(IC<1>{}, s + 1);
+      // the next tile's rows into the other slot (read after the barrier that
+      // starts the next tile)
+      store_row((k + 1) & 1, min(k + 1, ntiles - 1), pnext);
+
+      // acc[m][n][r]: row 32 (wv + 4 m) + lane % 32, column 32 n + 8 (r / 4) +
+      // 4 (lane / 32) + r % 4 of the tile.
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const int orow = outrow[32 * (wv + 4 * m) + (lane & 31)];
+        if (orow < 0) continue;
+        uint16_t *crow = g.c + (size_t)orow * g.ldc;
+#pragma unroll
+        for (int n = 0; n < (kGU ? NN / 2 : NN); ++n)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int col = n0 + 32 * n + 8 * gq + 4 * h;
+            if (col >= g.ncols) continue;
+            float o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if constexpr (kGU)
+                o[i] = swiglu(acc[m][n][4 * gq + i] * alpha, acc[m][n + NN / 2][4 * gq + i] * alpha);
+              else o[i] = acc[m][n][4 * gq + i] * alpha;
+            }
+            *reinterpret_cast<uint2 *>(crow + col) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+          }
+      }
+    };
+    if (nm == 2) run(IC<2>{});
+    else if (nm == 1) run(IC<1>{});
+    else run(IC<0>{});
+    __syncthreads();
   }
 }
 
