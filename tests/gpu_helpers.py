@@ -18,6 +18,8 @@ Tolerances (derived from the arithmetic, see the oracle's header):
 """
 from __future__ import annotations
 
+import ctypes
+
 import numpy as np
 import torch
 
@@ -75,9 +77,22 @@ def shared_of(d: dict):
     return (d["sgu"], d["sdown"]) if "sgu" in d else None
 
 
+def hip_events(n):
+    """n hipEvent_t handles (a ctypes array) from the HIP runtime."""
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    arr = (ctypes.c_void_p * n)()
+    for i in range(n):
+        ev = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(ev)) == 0
+        arr[i] = ev
+    return arr
+
+
 def run_block(binding, inp: dict, path: str = "decode", forced=None, want_debug=True,
-              ws=None):
-    """Runs the HIP path on `inp`; returns host arrays of out and intermediates."""
+              ws=None, stage_events=None):
+    """Runs the HIP path on `inp`; returns host arrays of out and intermediates.
+    stage_events: optional hipEvent_t array recorded around every stage."""
     cfg = inp["cfg"]
     M, H, E, I, SI, k = cfg["M"], cfg["H"], cfg["E"], cfg["I"], cfg["SI"], cfg["top_k"]
     d = device_inputs(inp)
@@ -95,6 +110,9 @@ def run_block(binding, inp: dict, path: str = "decode", forced=None, want_debug=
         dbg = dict(dbg or {})
         dbg["ids_in"] = dev(np.ascontiguousarray(forced[0], dtype=np.int32))
         dbg["tw_in"] = dev(np.ascontiguousarray(forced[1], dtype=np.float32))
+    if stage_events is not None:
+        dbg = dict(dbg or {})
+        dbg["stage_events"] = stage_events
     x = d["x"]
     out = torch.empty((M, H), dtype=torch.int16, device="cuda")
     fn = {"decode": binding.flint_moe_decode, "grouped": binding.flint_moe_grouped,

@@ -71,6 +71,20 @@ def test_grouped_forced_routing_and_determinism():
     assert np.array_equal(rf["out"], out_c)
 
 
+def test_grouped_side_stream_matches_serial():
+    """Without stage events the shared expert's GEMMs run on a second stream;
+    with them every stage runs in order on the caller's stream.  The bits
+    are the same either way, call after call."""
+    _say("grouped: side stream vs serial stages")
+    inp = synth.make_small(703, M=300, H=512, E=16, I=256, SI=192, top_k=4, router_std=0.3)
+    r1 = G.run_block(fm, inp, "grouped")
+    r2 = G.run_block(fm, inp, "grouped", stage_events=G.hip_events(fm.FLINT_STAGE_EVENTS))
+    r3 = G.run_block(fm, inp, "grouped")
+    for key in r1:
+        assert np.array_equal(r1[key], r2[key]), key
+        assert np.array_equal(r1[key], r3[key]), key
+
+
 def test_grouped_agrees_with_decode():
     """Both paths implement the same rule: same routing bit for bit where
     the logits agree, and outputs within the end-to-end tolerance."""
