@@ -97,6 +97,24 @@ def f32_to_bf16(vals) -> np.ndarray:
     return np.array([f(float(x)) for x in v.ravel()], dtype=np.uint16).reshape(v.shape)
 
 
+def f64_to_bf16(vals) -> np.ndarray:
+    """fp64 -> bf16 bits, one round to nearest even (no double rounding).
+
+    The value goes to fp32 first; when that lands exactly halfway between
+    two bf16 values without being exact, the fp32 bits are moved one step
+    toward the fp64 value so the bf16 rounding goes the way the fp64 value
+    lies (finite values)."""
+    x = np.asarray(vals, dtype=np.float64)
+    f = x.astype(np.float32)
+    b = f.view(np.uint32).copy()
+    tie = (b & 0xFFFF) == 0x8000
+    inexact = f.astype(np.float64) != x
+    away = np.abs(x) > np.abs(f.astype(np.float64))
+    nudge = tie & inexact
+    b = np.where(nudge & away, b + 1, np.where(nudge & ~away, b - 1, b)).astype(np.uint32)
+    return f32_to_bf16(b.view(np.float32))
+
+
 def e2m1(code: int) -> float:
     return lib().orc_e2m1(int(code))
 
@@ -228,6 +246,29 @@ def shared_expert(x, sgu, sdown, want_detail: bool = False):
     if want_detail:
         return sact, r2[0], dict(gate_up=r1[1], down=r2[1])
     return sact, r2
+
+
+def add_rms_norm(a, r, w, eps: float):
+    """Residual add and RMS norm in front of the block (page
+    "vllm.models.flint.ops.moe", _add_rms_norm and flint_moe_ll): for each
+    row, s = a + r in fp32 (one fp32 rounding of two bf16 values);
+    residual' = bf16(s); xn = bf16(s * rsqrt(mean(s^2) + eps) * w).  The
+    pages reduce mean(s^2) in fp32 in an order they do not fix and leave
+    their rsqrt helper unprinted; here the mean, the reciprocal square root
+    and the products are exact (fp64), rounded once to bf16.
+
+    a, r: [M, H] bf16 bits; w: [H] bf16 bits.  Returns (residual', xn) as
+    bf16 bits."""
+    af = bf16_to_f32(a)
+    rf = bf16_to_f32(r)
+    s = (af + rf).astype(np.float32)  # IEEE fp32 addition, round to nearest even
+    res = f32_to_bf16(s)
+    s64 = s.astype(np.float64)
+    H = s64.shape[-1]
+    ms = np.sum(s64 * s64, axis=-1, keepdims=True) / H
+    inv = 1.0 / np.sqrt(ms + np.float64(np.float32(eps)))
+    xn = f64_to_bf16(s64 * inv * bf16_to_f32(w).astype(np.float64))
+    return res, xn
 
 
 def moe_block(inp: dict, tokens=None, forced_ids=None, forced_tw=None,
