@@ -162,6 +162,25 @@ int flint_moe_decode(const uint16_t *x, const uint16_t *router,
                      const flint_moe_debug *dbg, void *ws, size_t ws_bytes,
                      void *stream);
 
+/* The decode MoE block behind a residual add and RMS norm (page
+ * "vllm.models.flint.ops.moe", flint_moe_ll with _add_rms_norm):
+ *   s = fp32(attn_out) + fp32(residual)          (one fp32 rounding)
+ *   residual_out = bf16(s)
+ *   xn_out = bf16((s * rsqrt(mean_h(s^2) + eps)) * ln_weight)   (fp32)
+ *   out = flint_moe_decode(xn_out, ...)
+ * attn_out, residual, residual_out, xn_out [M, H] bf16 (caller-owned, 16-byte
+ * aligned; xn_out is both a result and the block's input); ln_weight [H]
+ * bf16; eps >= 0; H % 8 == 0.  The other arguments, limits and errors are
+ * those of flint_moe_decode; nothing is written when an argument is
+ * rejected.  Inputs are not modified. */
+int flint_moe_ll(const uint16_t *attn_out, const uint16_t *residual,
+                 const uint16_t *ln_weight, float eps, const uint16_t *router,
+                 const flint_nvfp4_experts *w, const flint_shared_expert *shared,
+                 int M, int H, int E, int I, int top_k, uint16_t *out,
+                 uint16_t *residual_out, uint16_t *xn_out,
+                 const flint_moe_debug *dbg, void *ws, size_t ws_bytes,
+                 void *stream);
+
 /* The MoE block on NVFP4 experts for any M >= 1 with grouped MFMA GEMMs
  * (page "vllm.models.flint.ops.moe", flint_moe, grouped branch). */
 int flint_moe_grouped(const uint16_t *x, const uint16_t *router,

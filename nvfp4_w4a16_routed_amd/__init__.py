@@ -29,7 +29,7 @@ STATUS = {0: "FLINT_OK", -1: "FLINT_ERR_NULL", -2: "FLINT_ERR_SHAPE", -3: "FLINT
 EXPORTS = ("flint_status_str", "flint_last_hip_error", "flint_moe_workspace_bytes",
            "flint_moe_workspace_init", "flint_nvfp4_dequant", "flint_moe_topk",
            "flint_moe_route", "flint_moe_decode", "flint_moe_grouped",
-           "flint_moe_bf16_decode")
+           "flint_moe_bf16_decode", "flint_moe_ll")
 
 
 class FlintError(RuntimeError):
@@ -99,6 +99,9 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.restype = I32
             fn.argtypes = moe_args
+        L.flint_moe_ll.restype = I32
+        L.flint_moe_ll.argtypes = [P, P, P, ctypes.c_float, P, P, P, I32, I32, I32, I32, I32, P, P, P,
+                                   P, P, ctypes.c_size_t, P]
         _lib = L
     return _lib
 
@@ -223,6 +226,27 @@ def flint_moe_decode(x, router, experts: dict, shared, top_k: int, ws, out=None,
     E, I = experts["w13"].shape[0], experts["w2"].shape[2] * 2
     st = nvfp4_experts_struct(*(experts[k] for k in ("w13", "s13", "a13", "w2", "s2", "a2")))
     return _moe_call("flint_moe_decode", st, x, router, shared, I, E, top_k, ws, out, debug, stream)
+
+
+def flint_moe_ll(attn_out, residual, ln_weight, eps: float, router, experts: dict, shared, top_k: int,
+                 ws, out=None, residual_out=None, xn_out=None, debug=None, stream=None):
+    """Residual add + RMS norm, then the decode block on the normed rows.
+    Returns (out, residual_out, xn_out); outputs are allocated when None."""
+    M, H = attn_out.shape
+    E, I = experts["w13"].shape[0], experts["w2"].shape[2] * 2
+    st = nvfp4_experts_struct(*(experts[k] for k in ("w13", "s13", "a13", "w2", "s2", "a2")))
+    out = _new((M, H), attn_out.dtype, attn_out) if out is None else out
+    residual_out = _new((M, H), attn_out.dtype, attn_out) if residual_out is None else residual_out
+    xn_out = _new((M, H), attn_out.dtype, attn_out) if xn_out is None else xn_out
+    sh = _shared_struct(shared)
+    dbg = _debug_struct(debug)
+    rc = lib().flint_moe_ll(_ptr(attn_out), _ptr(residual), _ptr(ln_weight), float(eps), _ptr(router),
+                            ctypes.byref(st), ctypes.byref(sh) if sh else None, M, H, E, I, top_k,
+                            _ptr(out), _ptr(residual_out), _ptr(xn_out),
+                            ctypes.byref(dbg) if dbg else None, _ptr(ws), ws.numel() * ws.element_size(),
+                            _stream(stream))
+    _check("flint_moe_ll", rc)
+    return out, residual_out, xn_out
 
 
 def flint_moe_grouped(x, router, experts: dict, shared, top_k: int, ws, out=None, debug=None,

@@ -240,6 +240,39 @@ int flint_moe_decode(const uint16_t *x, const uint16_t *router, const flint_nvfp
                     H, E, I, top_k, out, dbg, ws, ws_bytes, (hipStream_t)stream);
 }
 
+int flint_moe_ll(const uint16_t *attn_out, const uint16_t *residual, const uint16_t *ln_weight,
+                 float eps, const uint16_t *router, const flint_nvfp4_experts *w,
+                 const flint_shared_expert *shared, int M, int H, int E, int I, int top_k,
+                 uint16_t *out, uint16_t *residual_out, uint16_t *xn_out,
+                 const flint_moe_debug *dbg, void *ws, size_t ws_bytes, void *stream) {
+  int st = check_common(M, H, E, I, top_k);
+  if (st) return st;
+  if (!add_rmsnorm_supported(H) || !(eps >= 0.0f) || eps > 3.0e38f) return FLINT_ERR_SHAPE;
+  if (M == 0) return FLINT_OK;  // nothing to compute; no pointer is used
+  if (!attn_out || !residual || !ln_weight || !residual_out || !xn_out) return FLINT_ERR_NULL;
+  if (!aligned16(attn_out) || !aligned16(residual) || !aligned16(ln_weight) ||
+      !aligned16(residual_out) || !aligned16(xn_out))
+    return FLINT_ERR_ALIGN;
+  // flint_moe_decode's own checks, before anything is queued
+  const bool forced = dbg && dbg->ids_in;
+  if (!w || !out || (!forced && !router)) return FLINT_ERR_NULL;
+  if (!w->w13 || !w->s13 || !w->a13 || !w->w2 || !w->s2 || !w->a2) return FLINT_ERR_NULL;
+  if (forced && !dbg->tw_in) return FLINT_ERR_NULL;
+  if (!ws) return FLINT_ERR_WORKSPACE;
+  if ((st = check_shared(shared, H, I))) return st;
+  if (carve_workspace(nullptr, M, H, E, I, shared && shared->w_gu ? shared->SI : 0, top_k).bytes > ws_bytes)
+    return FLINT_ERR_WORKSPACE;
+  if ((router && !aligned16(router)) || !aligned16(out) || !aligned16(ws) || !aligned16(w->w13) ||
+      !aligned16(w->s13) || !aligned16(w->a13) || !aligned16(w->w2) || !aligned16(w->s2) ||
+      !aligned16(w->a2))
+    return FLINT_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  if (hipError_t e = launch_add_rmsnorm(attn_out, residual, ln_weight, eps, M, H, residual_out, xn_out, s);
+      e != hipSuccess)
+    return hip_status(e);
+  return flint_moe_decode(xn_out, router, w, shared, M, H, E, I, top_k, out, dbg, ws, ws_bytes, stream);
+}
+
 int flint_moe_bf16_decode(const uint16_t *x, const uint16_t *router, const flint_bf16_experts *w,
                           const flint_shared_expert *shared, int M, int H, int E, int I,
                           int top_k, uint16_t *out, const flint_moe_debug *dbg, void *ws,

@@ -139,4 +139,10 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st);
 // Whether the grouped kernels handle these sizes.
 bool grouped_shape_supported(int H, int I, int SI);
 
+// Residual add + RMS norm rows (norm.hip): res_out = bf16(a + r), xn_out =
+// bf16((s * rsqrt(mean(s^2) + eps)) * w) for M rows of H.
+bool add_rmsnorm_supported(int H);
+hipError_t launch_add_rmsnorm(const uint16_t *a, const uint16_t *r, const uint16_t *w, float eps, int M,
+                              int H, uint16_t *res_out, uint16_t *xn_out, hipStream_t st);
+
 }  // namespace flint

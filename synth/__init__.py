@@ -204,3 +204,13 @@ def make_small(seed: int, M: int, H: int, E: int, I: int, SI: int, top_k: int,
         d["sgu"] = bf16_normal(seed, T_SGU, (2 * SI, H), 0.02)
         d["sdown"] = bf16_normal(seed, T_SDOWN, (H, SI), 0.02)
     return d
+
+
+def make_ll_inputs(seed: int, M: int, H: int) -> dict:
+    """Inputs of the residual-add RMS norm in front of the block: attn_out
+    ~ N(0, 1) and residual ~ N(0, 4) as [M, H] bf16 bits, ln_weight = 1 +
+    N(0, 0.1) as [H] bf16 bits, eps = 1e-6."""
+    attn = bf16_normal(seed, 101, (M, H), 1.0)
+    res = bf16_normal(seed, 102, (M, H), 4.0)
+    lw = to_bf16_bits(1.0 + bf16_bits_to_f32(bf16_normal(seed, 103, (H,), 0.1)).astype(np.float64))
+    return dict(attn_out=attn, residual=res, ln_weight=lw, eps=1e-6)

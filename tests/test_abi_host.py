@@ -88,6 +88,25 @@ def test_decode_rejects_bad_arguments():
     assert _decode(M=0, x=None) == 0       # empty batch: valid no-op
 
 
+def _ll(a=A, r=A, lw=A, eps=1e-6, M=8, H=2048, res=A, xn=A, ws_bytes=1 << 30):
+    w = _experts()
+    return fm.lib().flint_moe_ll(a, r, lw, eps, A, ctypes.byref(w), None, M, H, 128, 768, 8, A, res,
+                                 xn, None, A, ws_bytes, None)
+
+
+def test_ll_rejects_bad_arguments():
+    for kw in (dict(a=None), dict(r=None), dict(lw=None), dict(res=None), dict(xn=None)):
+        assert _ll(**kw) == -1, kw
+    assert _ll(eps=-1.0) == -2
+    assert _ll(eps=float("nan")) == -2
+    assert _ll(M=65) == -2                 # the decode block's limit
+    assert _ll(H=1000) == -2
+    assert _ll(a=MIS) == -3
+    assert _ll(xn=MIS) == -3
+    assert _ll(ws_bytes=1024) == -4        # rejected before the norm is queued
+    assert _ll(M=0, a=None) == 0           # empty batch: valid no-op
+
+
 def test_bf16_decode_and_grouped_reject_bad_arguments():
     L = fm.lib()
     w = fm.Bf16Experts(A, None)
