@@ -44,6 +44,7 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-grouped", action="store_true", help="skip the M=4096 grouped line")
+    ap.add_argument("--no-ll", action="store_true", help="skip the flint_moe_ll line")
     ap.add_argument("--grouped-steps", type=int, default=30)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain fp32 copy of MIB MiB 5 times (HBM counter scale)")
@@ -196,6 +197,11 @@ def run(fm, synth, torch, cfg_idx: int, path: str, steps: int, warmup: int, laye
     lays = [base] + [{kk: v.clone() for kk, v in base.items()} for _ in range(L - 1)]
     x = up(inp["x"])
     del inp
+    if path == "ll":  # the residual-add RMS norm inputs in front of the block
+        lli = synth.make_ll_inputs(1, M, H)
+        la, lr, lw = up(lli["attn_out"]), up(lli["residual"]), up(lli["ln_weight"])
+        lres = torch.empty((M, H), dtype=torch.int16, device=dev)
+        lxn = torch.empty((M, H), dtype=torch.int16, device=dev)
     out = torch.empty((M, H), dtype=torch.int16, device=dev)
     ws = fm.make_workspace(M, H, E, I, SI, k)
     ids = torch.empty((M, k), dtype=torch.int32, device=dev)
@@ -203,7 +209,7 @@ def run(fm, synth, torch, cfg_idx: int, path: str, steps: int, warmup: int, laye
     sp = ctypes.c_void_p(stream.cuda_stream)
     lib = fm.lib()
     fn = {"decode": lib.flint_moe_decode, "grouped": lib.flint_moe_grouped,
-          "bf16_decode": lib.flint_moe_bf16_decode}[path]
+          "bf16_decode": lib.flint_moe_bf16_decode, "ll": lib.flint_moe_ll}[path]
     keep = []
 
     def c_args(lay, dbg=None):
@@ -213,6 +219,11 @@ def run(fm, synth, torch, cfg_idx: int, path: str, steps: int, warmup: int, laye
             w = fm.Bf16Experts(fm._ptr(lay["bw13"]), fm._ptr(lay["bw2"]))
         sh = fm.SharedExpert(fm._ptr(lay["sgu"]), fm._ptr(lay["sdown"]), SI)
         keep.extend([w, sh, dbg])
+        if path == "ll":
+            return (fm._ptr(la), fm._ptr(lr), fm._ptr(lw), ctypes.c_float(lli["eps"]),
+                    fm._ptr(lay["router"]), ctypes.byref(w), ctypes.byref(sh), M, H, E, I, k,
+                    fm._ptr(out), fm._ptr(lres), fm._ptr(lxn),
+                    ctypes.byref(dbg) if dbg is not None else None, fm._ptr(ws), ws.numel(), sp)
         return (fm._ptr(x), fm._ptr(lay["router"]), ctypes.byref(w), ctypes.byref(sh), M, H, E,
                 I, k, fm._ptr(out), ctypes.byref(dbg) if dbg is not None else None, fm._ptr(ws),
                 ws.numel(), sp)
@@ -337,6 +348,14 @@ def main():
         inp = synth.make_inputs(cfg_idx)
         res["cpu_baseline"] = cpu_baseline(inp, a.cpu_seconds)
         del inp
+    if path == "decode" and not a.no_ll:
+        # flint_moe_ll on the same workload: the residual-add RMS norm in
+        # front of the same decode block, same protocol and weight rotation
+        ll = run(fm, synth, torch, cfg_idx, "ll", a.steps, a.warmup, a.layers)
+        res["ll"] = {"entry": "flint_moe_ll", "workload": ll["cfg"]["name"],
+                     "us_per_call": round(ll["ms_step"] * 1e3, 3),
+                     "decode_us_per_call": round(r["ms_step"] * 1e3, 3),
+                     "tokens_per_s": round(M / (ll["ms_step"] * 1e-3), 1)}
     if not a.no_grouped and path != "grouped":
         g = run(fm, synth, torch, 4, "grouped", a.grouped_steps, 3, 1)
         gc = g["cfg"]
