@@ -85,11 +85,20 @@ typedef struct {
 
 /* Ungated shared SwiGLU expert (page "vllm.models.flint.model": Flint has
  * an ungated shared expert added to the routed sum).  w_gu == NULL means no
- * shared expert (its output is taken as 0). */
+ * shared expert (its output is taken as 0).
+ * Precomputed shared output (page "vllm.models.flint.ops.moe", flint_moe's
+ * shared_output / shared_ready): when sh_in != NULL the block computes no
+ * shared expert (w_gu, w_down and SI are ignored) and adds sh_in [M, H]
+ * bf16 (16-byte aligned) in its place, out = bf16(bf16(routed) + sh_in);
+ * sh_ready, a hipEvent_t or NULL, is waited on by the call's stream just
+ * before sh_in is read, so the producer may still be running when the call
+ * is made. */
 typedef struct {
   const uint16_t *w_gu;   /* [2*SI, H] bf16, rows 0..SI-1 gate, SI..2SI-1 up */
   const uint16_t *w_down; /* [H, SI] bf16 */
   int SI;
+  const uint16_t *sh_in;  /* NULL, or the precomputed shared output [M, H] */
+  void *sh_ready;         /* NULL, or a hipEvent_t completing sh_in */
 } flint_shared_expert;
 
 /* Optional inputs and outputs of the MoE entry points; NULL = unused.

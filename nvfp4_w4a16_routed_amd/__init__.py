@@ -54,7 +54,7 @@ class Bf16Experts(ctypes.Structure):
 
 
 class SharedExpert(ctypes.Structure):
-    _fields_ = [("w_gu", P), ("w_down", P), ("SI", I32)]
+    _fields_ = [("w_gu", P), ("w_down", P), ("SI", I32), ("sh_in", P), ("sh_ready", P)]
 
 
 FLINT_STAGE_EVENTS = 8
@@ -186,8 +186,12 @@ def flint_moe_route(x, router, top_k: int, ws, logits=None, ids=None, tw=None, s
 
 
 def _shared_struct(shared):
+    """shared: (w_gu, w_down), or dict(sh_in=[M, H] tensor, sh_ready=hipEvent_t
+    handle or None) for a precomputed shared output, or None."""
     if shared is None:
         return None
+    if isinstance(shared, dict):
+        return SharedExpert(None, None, 0, _ptr(shared["sh_in"]), shared.get("sh_ready"))
     gu, down = shared
     return SharedExpert(_ptr(gu), _ptr(down), int(gu.shape[0]) // 2)
 

@@ -79,6 +79,7 @@ int check_common(int M, int H, int E, int I, int top_k) {
 }
 
 int check_shared(const flint_shared_expert *sh, int H, int I) {
+  if (sh && sh->sh_in) return aligned16(sh->sh_in) ? FLINT_OK : FLINT_ERR_ALIGN;
   if (!sh || !sh->w_gu) return FLINT_OK;
   if (!sh->w_down) return FLINT_ERR_NULL;
   if (!aligned16(sh->w_gu) || !aligned16(sh->w_down)) return FLINT_ERR_ALIGN;
@@ -93,7 +94,8 @@ int run_decode(int fmt, const uint16_t *x, const uint16_t *router, const void *w
                const float *a2, const flint_shared_expert *shared, int M, int H, int E, int I,
                int top_k, uint16_t *out, const flint_moe_debug *dbg, void *ws,
                size_t ws_bytes, hipStream_t st) {
-  const bool has_shared = shared && shared->w_gu;
+  const bool ext_sh = shared && shared->sh_in;  // precomputed shared output
+  const bool has_shared = !ext_sh && shared && shared->w_gu;
   const int SI = has_shared ? shared->SI : 0;
   Workspace W = carve_workspace(ws, M, H, E, I, SI, top_k);
   if (W.bytes > ws_bytes) return FLINT_ERR_WORKSPACE;
@@ -143,6 +145,11 @@ int run_decode(int fmt, const uint16_t *x, const uint16_t *router, const void *w
   // One kernel runs every stage: the stage events bracket the whole of it.
   hipError_t e = mark(0);
   if (e == hipSuccess) e = launch_decode(fmt, a, st);
+  // Precomputed shared output: the kernel ran without a shared expert, so
+  // out holds bf16(routed) exactly; the rule's last step adds sh_in.
+  if (e == hipSuccess && ext_sh && shared->sh_ready)
+    e = hipStreamWaitEvent(st, (hipEvent_t)shared->sh_ready, 0);
+  if (e == hipSuccess && ext_sh) e = launch_add_bf16(out, shared->sh_in, (size_t)M * H, st);
   for (int i = 1; i < FLINT_STAGE_EVENTS && e == hipSuccess; ++i) e = mark(i);
   return hip_status(e);
 }
@@ -298,7 +305,8 @@ int flint_moe_grouped(const uint16_t *x, const uint16_t *router, const flint_nvf
                       uint16_t *out, const flint_moe_debug *dbg, void *ws, size_t ws_bytes,
                       void *stream) {
   const bool forced = dbg && dbg->ids_in;
-  const bool has_shared = shared && shared->w_gu;
+  const bool ext_sh = shared && shared->sh_in;  // precomputed shared output
+  const bool has_shared = !ext_sh && shared && shared->w_gu;
   const int SI = has_shared ? shared->SI : 0;
   if (M < 0 || top_k < 1 || E < 1 || top_k > E || E > kMaxExperts) return FLINT_ERR_SHAPE;
   if ((long)M * top_k > (long)1 << 30) return FLINT_ERR_SHAPE;
@@ -312,7 +320,8 @@ int flint_moe_grouped(const uint16_t *x, const uint16_t *router, const flint_nvf
   if (!aligned16(x) || (router && !aligned16(router)) || !aligned16(out) || !aligned16(ws) ||
       !aligned16(w->w13) || !aligned16(w->s13) || !aligned16(w->a13) || !aligned16(w->w2) ||
       !aligned16(w->s2) || !aligned16(w->a2) ||
-      (has_shared && (!aligned16(shared->w_gu) || !aligned16(shared->w_down))))
+      (has_shared && (!aligned16(shared->w_gu) || !aligned16(shared->w_down))) ||
+      (ext_sh && !aligned16(shared->sh_in)))
     return FLINT_ERR_ALIGN;
   Workspace W = carve_workspace(ws, M, H, E, I, SI, top_k);
   if (W.bytes > ws_bytes) return FLINT_ERR_WORKSPACE;
@@ -328,6 +337,8 @@ int flint_moe_grouped(const uint16_t *x, const uint16_t *router, const flint_nvf
   a.a2 = w->a2;
   a.sgu = has_shared ? shared->w_gu : nullptr;
   a.sdown = has_shared ? shared->w_down : nullptr;
+  a.sh_ext = ext_sh ? shared->sh_in : nullptr;
+  a.sh_ready = ext_sh ? shared->sh_ready : nullptr;
   a.ids_in = forced ? dbg->ids_in : nullptr;
   a.logits = (dbg && dbg->logits_out) ? dbg->logits_out : W.logits;
   int32_t *ids = (dbg && dbg->ids_out) ? dbg->ids_out : W.ids;

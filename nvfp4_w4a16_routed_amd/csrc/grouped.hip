@@ -976,12 +976,16 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
   } else if (a.sgu) {
     if ((err = shared_down()) != hipSuccess) return err;
   }
-  // 7. combine + shared add
+  // 7. combine + shared add (a precomputed shared output: once its event
+  // has completed)
   if ((err = mark(6)) != hipSuccess) return err;
+  if (a.sh_ext && a.sh_ready && (err = hipStreamWaitEvent(st, (hipEvent_t)a.sh_ready, 0)) != hipSuccess)
+    return err;
   {
     const long n = (long)M * (H / 8);
+    const uint16_t *shp = a.sh_ext ? a.sh_ext : (a.sgu ? a.sh : nullptr);
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.y, a.tw,
-                       a.ids, a.sgu ? a.sh : nullptr, M, H, E, k, a.out);
+                       a.ids, shp, M, H, E, k, a.out);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   return mark(7);

@@ -122,6 +122,8 @@ struct GroupedArgs {
   const uint8_t *w2, *s2;
   const float *a2;
   const uint16_t *sgu, *sdown;  // shared expert (bf16), NULL = none
+  const uint16_t *sh_ext;       // precomputed shared output [M, H] (then sgu is NULL), or NULL
+  void *sh_ready;               // hipEvent_t completing sh_ext, or NULL
   const int32_t *ids_in;        // forced routing, NULL = route
   uint16_t *logits;             // [M, E]
   int32_t *ids;                 // [M, k] (ids_in when forced)
@@ -142,6 +144,8 @@ bool grouped_shape_supported(int H, int I, int SI);
 // Residual add + RMS norm rows (norm.hip): res_out = bf16(a + r), xn_out =
 // bf16((s * rsqrt(mean(s^2) + eps)) * w) for M rows of H.
 bool add_rmsnorm_supported(int H);
+// out[i] = bf16(fp32(out[i]) + fp32(sh[i])) for n bf16 values (n % 8 == 0).
+hipError_t launch_add_bf16(uint16_t *out, const uint16_t *sh, size_t n, hipStream_t st);
 hipError_t launch_add_rmsnorm(const uint16_t *a, const uint16_t *r, const uint16_t *w, float eps, int M,
                               int H, uint16_t *res_out, uint16_t *xn_out, hipStream_t st);
 

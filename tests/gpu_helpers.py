@@ -89,6 +89,14 @@ def hip_events(n):
     return arr
 
 
+def hip_record(ev, stream=None):
+    """hipEventRecord(ev, stream) (default: torch's current stream)."""
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    st = (stream or torch.cuda.current_stream()).cuda_stream
+    assert hip.hipEventRecord(ev, ctypes.c_void_p(st)) == 0
+
+
 def run_block(binding, inp: dict, path: str = "decode", forced=None, want_debug=True,
               ws=None, stage_events=None):
     """Runs the HIP path on `inp`; returns host arrays of out and intermediates.

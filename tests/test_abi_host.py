@@ -83,6 +83,8 @@ def test_decode_rejects_bad_arguments():
     assert _decode(shared=sh) == -1
     sh = fm.SharedExpert(A, A, 700)
     assert _decode(shared=sh) == -2
+    sh = fm.SharedExpert(None, None, 0, MIS, None)
+    assert _decode(shared=sh) == -3        # precomputed shared output, misaligned
     dbg = fm.MoeDebug(A, None, None, None, None, None, None, None, None)
     assert _decode(dbg=dbg) == -1          # forced ids without weights
     assert _decode(M=0, x=None) == 0       # empty batch: valid no-op
