@@ -99,6 +99,14 @@ typedef struct {
   int SI;
   const uint16_t *sh_in;  /* NULL, or the precomputed shared output [M, H] */
   void *sh_ready;         /* NULL, or a hipEvent_t completing sh_in */
+  /* NVFP4 shared expert (page "vllm.models.flint.ops.moe": E4M3 block scales
+   * and one fp32 global scale per matrix; computed as a routed expert with
+   * E = 1, the same rule as the routed experts).  When s_gu != NULL, w_gu
+   * holds E2M1 codes [2*SI, H/2] (bytes), s_gu [2*SI, H/16], a_gu -> the
+   * device fp32 global scale, w_down codes [H, SI/2], s_down [H, SI/16],
+   * a_down.  Grouped path only: the decode entry points reject it. */
+  const uint8_t *s_gu, *s_down;
+  const float *a_gu, *a_down;
 } flint_shared_expert;
 
 /* Optional inputs and outputs of the MoE entry points; NULL = unused.

@@ -54,7 +54,8 @@ class Bf16Experts(ctypes.Structure):
 
 
 class SharedExpert(ctypes.Structure):
-    _fields_ = [("w_gu", P), ("w_down", P), ("SI", I32), ("sh_in", P), ("sh_ready", P)]
+    _fields_ = [("w_gu", P), ("w_down", P), ("SI", I32), ("sh_in", P), ("sh_ready", P),
+                ("s_gu", P), ("s_down", P), ("a_gu", P), ("a_down", P)]
 
 
 FLINT_STAGE_EVENTS = 8
@@ -190,8 +191,12 @@ def _shared_struct(shared):
     handle or None) for a precomputed shared output, or None."""
     if shared is None:
         return None
-    if isinstance(shared, dict):
+    if isinstance(shared, dict) and "sh_in" in shared:
         return SharedExpert(None, None, 0, _ptr(shared["sh_in"]), shared.get("sh_ready"))
+    if isinstance(shared, dict):  # NVFP4 shared expert (grouped path)
+        return SharedExpert(_ptr(shared["w13"]), _ptr(shared["w2"]), int(shared["w13"].shape[-2]) // 2, None,
+                            None, _ptr(shared["s13"]), _ptr(shared["s2"]), _ptr(shared["a13"]),
+                            _ptr(shared["a2"]))
     gu, down = shared
     return SharedExpert(_ptr(gu), _ptr(down), int(gu.shape[0]) // 2)
 

@@ -55,6 +55,8 @@ Workspace carve_workspace(void *base, int M, int H, int E, int I, int SI, int to
   w.sh = static_cast<uint16_t *>(take(2 * (size_t)M * H));
   w.lists = static_cast<int32_t *>(take(4 * (size_t)E * M));
   w.counts = static_cast<int32_t *>(take(4 * (size_t)E));
+  w.sh_lists = static_cast<int32_t *>(take(4 * (size_t)M));
+  w.sh_counts = static_cast<int32_t *>(take(16));
   w.bytes = off;
   return w;
 }
@@ -81,6 +83,7 @@ int check_common(int M, int H, int E, int I, int top_k) {
 int check_shared(const flint_shared_expert *sh, int H, int I) {
   if (sh && sh->sh_in) return aligned16(sh->sh_in) ? FLINT_OK : FLINT_ERR_ALIGN;
   if (!sh || !sh->w_gu) return FLINT_OK;
+  if (sh->s_gu) return FLINT_ERR_SHAPE;  // NVFP4 shared expert: grouped path only
   if (!sh->w_down) return FLINT_ERR_NULL;
   if (!aligned16(sh->w_gu) || !aligned16(sh->w_down)) return FLINT_ERR_ALIGN;
   if (!decode_shape_supported(H, sh->SI)) return FLINT_ERR_SHAPE;
@@ -316,6 +319,11 @@ int flint_moe_grouped(const uint16_t *x, const uint16_t *router, const flint_nvf
   if (!w->w13 || !w->s13 || !w->a13 || !w->w2 || !w->s2 || !w->a2) return FLINT_ERR_NULL;
   if (forced && !dbg->tw_in) return FLINT_ERR_NULL;
   if (has_shared && !shared->w_down) return FLINT_ERR_NULL;
+  const bool nv_sh = has_shared && shared->s_gu;
+  if (nv_sh && (!shared->s_down || !shared->a_gu || !shared->a_down)) return FLINT_ERR_NULL;
+  if (nv_sh && (!aligned16(shared->s_gu) || !aligned16(shared->s_down) || !aligned16(shared->a_gu) ||
+                !aligned16(shared->a_down)))
+    return FLINT_ERR_ALIGN;
   if (!ws) return FLINT_ERR_WORKSPACE;
   if (!aligned16(x) || (router && !aligned16(router)) || !aligned16(out) || !aligned16(ws) ||
       !aligned16(w->w13) || !aligned16(w->s13) || !aligned16(w->a13) || !aligned16(w->w2) ||
@@ -339,6 +347,12 @@ int flint_moe_grouped(const uint16_t *x, const uint16_t *router, const flint_nvf
   a.sdown = has_shared ? shared->w_down : nullptr;
   a.sh_ext = ext_sh ? shared->sh_in : nullptr;
   a.sh_ready = ext_sh ? shared->sh_ready : nullptr;
+  a.s_gu = nv_sh ? shared->s_gu : nullptr;
+  a.s_down = nv_sh ? shared->s_down : nullptr;
+  a.a_gu = nv_sh ? shared->a_gu : nullptr;
+  a.a_down = nv_sh ? shared->a_down : nullptr;
+  a.sh_lists = W.sh_lists;
+  a.sh_counts = W.sh_counts;
   a.ids_in = forced ? dbg->ids_in : nullptr;
   a.logits = (dbg && dbg->logits_out) ? dbg->logits_out : W.logits;
   int32_t *ids = (dbg && dbg->ids_out) ? dbg->ids_out : W.ids;

@@ -809,6 +809,14 @@ hipError_t launch_gemm(const GemmArgs &g, int row_tiles, int col_tiles, hipStrea
   return hipGetLastError();
 }
 
+// The NVFP4 shared expert's row list: rows 0..M-1 of one "expert".
+__global__ void __launch_bounds__(256) iota_list_kernel(int32_t *__restrict__ lists, int M,
+                                                        int32_t *__restrict__ counts) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < M) lists[i] = i;
+  if (i == 0) counts[0] = M;
+}
+
 // One block per CU (32 per XCD), more if an XCD's tiles would exceed
 // kMaxTiles per block (row_tiles bounds the actual count, known on the
 // device).
@@ -897,7 +905,40 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
     if ((err = hipStreamWaitEvent(sd->s, sd->fork, 0)) != hipSuccess) return err;
     sst = sd->s;
   }
+  // NVFP4 shared expert: the routed kernels with one expert whose list is
+  // every row (its codes, scales and global scale in place of W13 / W2)
+  auto nv_shared = [&](int mode) -> hipError_t {
+    GemmArgs g{};
+    g.top_k = 1;
+    g.lists = a.sh_lists;
+    g.counts = a.sh_counts;
+    g.list_stride = M;
+    g.E = 1;
+    g.a_rows = M;
+    if (mode == kRoutedGateUp) {
+      g.a = a.x;
+      g.b = reinterpret_cast<const uint8_t *>(a.sgu);
+      g.bs = a.s_gu;
+      g.alpha = a.a_gu;
+      g.c = a.sact;
+      g.K = H;
+      g.ncols = SI;
+      g.ldc = SI;
+      g.I = SI;
+      return launch_routed<kRoutedGateUp>(g, (M + kRBM - 1) / kRBM + 1, sst);
+    }
+    g.a = a.sact;
+    g.b = reinterpret_cast<const uint8_t *>(a.sdown);
+    g.bs = a.s_down;
+    g.alpha = a.a_down;
+    g.c = a.sh;
+    g.K = SI;
+    g.ncols = H;
+    g.ldc = H;
+    return launch_routed<kRoutedDown>(g, (M + kRBM - 1) / kRBM + 1, sst);
+  };
   auto shared_down = [&]() -> hipError_t {
+    if (a.s_gu) return nv_shared(kRoutedDown);
     GemmArgs sdn{};
     sdn.a = a.sact;
     sdn.b = reinterpret_cast<const uint8_t *>(a.sdown);
@@ -909,7 +950,15 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
     sdn.ldc = H;
     return launch_gemm<kSharedDown>(sdn, (M + kBM - 1) / kBM, H / kBN, sst);
   };
-  if (a.sgu) {
+  if (a.sgu && a.s_gu) {
+    hipLaunchKernelGGL(iota_list_kernel, dim3((M + 255) / 256), dim3(256), 0, sst, a.sh_lists, M, a.sh_counts);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = nv_shared(kRoutedGateUp)) != hipSuccess) return err;
+    if (side) {
+      if ((err = shared_down()) != hipSuccess) return err;
+      if ((err = hipEventRecord(sd->join, sst)) != hipSuccess) return err;
+    }
+  } else if (a.sgu) {
     GemmArgs s{};
     s.a = a.x;
     s.b = reinterpret_cast<const uint8_t *>(a.sgu);

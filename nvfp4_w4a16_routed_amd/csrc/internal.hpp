@@ -84,6 +84,8 @@ struct Workspace {
   uint16_t *sh;        // [M, H]
   int32_t *lists;      // [E, M] grouped pair lists
   int32_t *counts;     // [E]
+  int32_t *sh_lists;   // [M] rows 0..M-1: the NVFP4 shared expert's list (E = 1)
+  int32_t *sh_counts;  // [1]
   size_t bytes;        // total bytes used
 };
 
@@ -124,6 +126,10 @@ struct GroupedArgs {
   const uint16_t *sgu, *sdown;  // shared expert (bf16), NULL = none
   const uint16_t *sh_ext;       // precomputed shared output [M, H] (then sgu is NULL), or NULL
   void *sh_ready;               // hipEvent_t completing sh_ext, or NULL
+  // NVFP4 shared expert (then sgu / sdown hold E2M1 codes), else NULL
+  const uint8_t *s_gu, *s_down;
+  const float *a_gu, *a_down;
+  int32_t *sh_lists, *sh_counts;  // identity list of the M rows, for the routed kernel with E = 1
   const int32_t *ids_in;        // forced routing, NULL = route
   uint16_t *logits;             // [M, E]
   int32_t *ids;                 // [M, k] (ids_in when forced)

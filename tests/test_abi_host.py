@@ -85,6 +85,8 @@ def test_decode_rejects_bad_arguments():
     assert _decode(shared=sh) == -2
     sh = fm.SharedExpert(None, None, 0, MIS, None)
     assert _decode(shared=sh) == -3        # precomputed shared output, misaligned
+    sh = fm.SharedExpert(A, A, 768, None, None, A, A, A, A)
+    assert _decode(shared=sh) == -2        # an NVFP4 shared expert: grouped path only
     dbg = fm.MoeDebug(A, None, None, None, None, None, None, None, None)
     assert _decode(dbg=dbg) == -1          # forced ids without weights
     assert _decode(M=0, x=None) == 0       # empty batch: valid no-op

@@ -1,0 +1,54 @@
+"""An NVFP4 shared expert on the grouped path (page "vllm.models.flint.ops.moe":
+E4M3 block scales and one fp32 global scale per matrix, computed as a routed
+expert with E = 1), through the C ABI, against the oracle's routed steps with
+one expert that every token selects."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import gpu_helpers as G
+
+pytestmark = pytest.mark.gpu
+
+fm = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _binding():
+    global fm
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import nvfp4_w4a16_routed_amd as m
+    m.lib()
+    fm = m
+    oracle.set_threads(16)
+    yield
+
+
+@pytest.mark.parametrize("M,H,SI", [(300, 512, 256), (37, 256, 128)])
+def test_grouped_nvfp4_shared_expert(M, H, SI):
+    print(f"grouped NVFP4 shared expert M={M} H={H} SI={SI}", flush=True)
+    inp = synth.make_small(950 + M, M=M, H=H, E=16, I=SI, SI=0, top_k=4, router_std=0.3)
+    cfg = inp["cfg"]
+    E, I, k = cfg["E"], cfg["I"], cfg["top_k"]
+    shw = synth.nvfp4_experts(951 + M, 1, H, SI)
+    d = G.device_inputs(inp)
+    shd = {kk: G.dev(v) for kk, v in shw.items()}
+    ws = fm.make_workspace(M, H, E, I, SI, k)
+    z = lambda shape, dt: torch.empty(shape, dtype=dt, device="cuda")
+    dbg = dict(ids_out=z((M, k), torch.int32), tw_out=z((M, k), torch.float32),
+               y_out=z((M * k, H), torch.int16), sact_out=z((M, SI), torch.int16),
+               sh_out=z((M, H), torch.int16))
+    out = fm.flint_moe_grouped(d["x"], d["router"], G.experts_of(d), shd, k, ws, debug=dbg)
+    torch.cuda.synchronize()
+    one = np.zeros((M, 1), dtype=np.int32)
+    sact = G.host(dbg["sact_out"]).view(np.uint16)
+    ref_sact, det = oracle.gate_up(inp["x"], one, 1, shw, SI, want_detail=True)
+    G.check_act(sact, ref_sact, det, "nvfp4 shared gate/up")
+    sh = G.host(dbg["sh_out"]).view(np.uint16)
+    ref_sh, det2 = oracle.down(sact, one, shw, H, want_detail=True)
+    G.check_y(sh, ref_sh, det2, "nvfp4 shared down")
+    out_c, _ = oracle.combine(G.host(dbg["y_out"]).view(np.uint16), G.host(dbg["tw_out"]), sh, k)
+    assert np.array_equal(G.host(out).view(np.uint16), out_c)
