@@ -197,6 +197,10 @@ def run(fm, synth, torch, cfg_idx: int, path: str, steps: int, warmup: int, laye
     lays = [base] + [{kk: v.clone() for kk, v in base.items()} for _ in range(L - 1)]
     x = up(inp["x"])
     del inp
+    if path == "sh_in":  # a precomputed shared output in place of the shared expert
+        sh_buf = torch.zeros((M, H), dtype=torch.int16, device=dev)
+    if path == "nv_shared":  # an NVFP4 shared expert of the same shape
+        nvs = {kk: up(v) for kk, v in synth.nvfp4_experts(7, 1, H, SI).items()}
     if path == "ll":  # the residual-add RMS norm inputs in front of the block
         lli = synth.make_ll_inputs(1, M, H)
         la, lr, lw = up(lli["attn_out"]), up(lli["residual"]), up(lli["ln_weight"])
@@ -209,7 +213,8 @@ def run(fm, synth, torch, cfg_idx: int, path: str, steps: int, warmup: int, laye
     sp = ctypes.c_void_p(stream.cuda_stream)
     lib = fm.lib()
     fn = {"decode": lib.flint_moe_decode, "grouped": lib.flint_moe_grouped,
-          "bf16_decode": lib.flint_moe_bf16_decode, "ll": lib.flint_moe_ll}[path]
+          "bf16_decode": lib.flint_moe_bf16_decode, "ll": lib.flint_moe_ll,
+          "sh_in": lib.flint_moe_decode, "nv_shared": lib.flint_moe_grouped}[path]
     keep = []
 
     def c_args(lay, dbg=None):
@@ -218,6 +223,11 @@ def run(fm, synth, torch, cfg_idx: int, path: str, steps: int, warmup: int, laye
         else:
             w = fm.Bf16Experts(fm._ptr(lay["bw13"]), fm._ptr(lay["bw2"]))
         sh = fm.SharedExpert(fm._ptr(lay["sgu"]), fm._ptr(lay["sdown"]), SI)
+        if path == "sh_in":
+            sh = fm.SharedExpert(None, None, 0, fm._ptr(sh_buf), None)
+        if path == "nv_shared":
+            sh = fm.SharedExpert(fm._ptr(nvs["w13"]), fm._ptr(nvs["w2"]), SI, None, None, fm._ptr(nvs["s13"]),
+                                 fm._ptr(nvs["s2"]), fm._ptr(nvs["a13"]), fm._ptr(nvs["a2"]))
         keep.extend([w, sh, dbg])
         if path == "ll":
             return (fm._ptr(la), fm._ptr(lr), fm._ptr(lw), ctypes.c_float(lli["eps"]),
@@ -356,6 +366,12 @@ def main():
                      "us_per_call": round(ll["ms_step"] * 1e3, 3),
                      "decode_us_per_call": round(r["ms_step"] * 1e3, 3),
                      "tokens_per_s": round(M / (ll["ms_step"] * 1e-3), 1)}
+    if path == "decode" and not a.no_ll:
+        # the same call with a precomputed shared output (no shared expert
+        # computed; the output is added after the kernel)
+        so = run(fm, synth, torch, cfg_idx, "sh_in", a.steps, a.warmup, a.layers)
+        res["shared_output"] = {"entry": "flint_moe_decode + sh_in", "workload": so["cfg"]["name"],
+                                "us_per_call": round(so["ms_step"] * 1e3, 3)}
     if not a.no_grouped and path != "grouped":
         g = run(fm, synth, torch, 4, "grouped", a.grouped_steps, 3, 1)
         gc = g["cfg"]
@@ -379,6 +395,9 @@ def main():
                                                      "routed_gemm_kernel", gc["name"]),
                          "flops_per_launch": fl["gate_up"], "avg_launch_us": round(st[3] * 1e3, 2)},
         }
+        # the same workload with an NVFP4 shared expert (routed kernels, E = 1)
+        nv = run(fm, synth, torch, 4, "nv_shared", a.grouped_steps, 3, 1)
+        res["grouped"]["nvfp4_shared_ms_per_step"] = round(nv["ms_step"], 4)
     print(json.dumps(res), flush=True)
 
 
