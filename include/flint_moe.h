@@ -4,7 +4,7 @@
  * The block (vLLM page "vllm.models.flint.ops.moe", module docstring,
  * "Numerics"; page "vllm.models.flint.model", FlintSparseMoeBlock):
  *   logits = bf16(x @ router^T)                       (fp32 accumulation)
- *   ids    = top_k experts by logit (ties -> lowest expert index)
+ *   ids    = the top_k experts by logit, equal logits to the smaller index
  *   s_j    = fp32 sigmoid of the selected logits (exact exp, RN division)
  *   tw_j   = bf16(s_j / (sum_j s_j + 1e-20)), held in fp32
  *   per pair (t, j), expert e = ids[t, j]:
@@ -33,13 +33,20 @@
  *      decode entry points: M <= 64, M * top_k <= 512, (H, I) one of
  *        (2048, 768), (256, 128), (256, 256), (512, 128), (512, 256),
  *        shared width SI == I (or no shared expert);
- *      flint_moe_grouped: any M with M * top_k <= 2^30; H % 128 == 0,
- *        128 <= H <= 8192; I % 64 == 0, 64 <= I <= 8192; SI % 64 == 0,
- *        SI <= 8192 (0 = no shared expert);
+ *      flint_moe_grouped: H % 128 == 0, 128 <= H <= 8192; I % 64 == 0,
+ *        64 <= I <= 8192; a shared expert has SI % 64 == 0, 64 <= SI <=
+ *        8192; M * H * 2, M * top_k * I * 2 and M * SI * 2 bytes each
+ *        below 2^31 (the GEMMs address x, act and sact through 32-bit
+ *        buffer offsets);
  *      flint_moe_route: H in {256, 512, 1024, 2048, 4096}, M <= 16376.
  *  - A workspace is used by one stream at a time: its counters are reset by
  *    the kernels themselves, so launches using one workspace must be
  *    serialised on one stream (as the pages require of their route counter).
+ *  - The decode kernel needs all of its blocks resident at once (one per
+ *    compute unit).  The library orders its own decode launches on a device
+ *    one after another, also across streams; a caller must not run other
+ *    long kernels concurrently with a decode call on the same GPU (its waits
+ *    then give up: see flint_moe_wait_errors).
  */
 #ifndef FLINT_MOE_H
 #define FLINT_MOE_H
@@ -130,9 +137,32 @@ typedef struct {
    * 6 combine.  The decode entry points run one kernel: it is stage 0 and
    * the other stages take no time. */
   void **stage_events;
+  /* Decode entry points only (test hooks of the bounded waits; 0 = off):
+   * wait_polls > 0 caps every cross-block wait of the decode kernel at that
+   * many polls (default 2^20); wait_probe != 0 adds one wait on a word that
+   * nothing sets, which gives up and is reported by flint_moe_wait_errors
+   * (FLINT_WAIT_PROBE).  A call whose wait gave up still ends, but its
+   * results are not valid. */
+  int wait_polls;
+  int wait_probe;
 } flint_moe_debug;
 
 #define FLINT_STAGE_EVENTS 8
+
+/* Kinds of bounded waits of the decode kernel, as bits of the word that
+ * flint_moe_wait_errors returns.  The decode kernel runs one block per
+ * compute unit and its blocks wait for each other's results; each wait is
+ * bounded so the kernel always ends, and a wait that gives up sets its bit.
+ * A set bit means a call's results are not valid: the grid was not fully
+ * resident (another kernel held compute units for the whole wait), or the
+ * workspace was used by two streams at once. */
+#define FLINT_WAIT_LOGITS 1         /* a token's router logits */
+#define FLINT_WAIT_SHARED_GATE_UP 2 /* the shared expert's gate/up blocks */
+#define FLINT_WAIT_GATE_UP 4        /* a routed expert's gate/up blocks */
+#define FLINT_WAIT_COMBINE_SHARED 8 /* the shared down blocks of a combine item */
+#define FLINT_WAIT_COMBINE_DOWN 16  /* the routed down blocks of a combine item */
+#define FLINT_WAIT_LDS 32           /* a wave of the same block */
+#define FLINT_WAIT_PROBE 64         /* the test hook (flint_moe_debug.wait_probe) */
 
 /* Status code -> static string. */
 const char *flint_status_str(int status);
@@ -169,6 +199,12 @@ int flint_moe_topk(const uint16_t *logits, int M, int E, int top_k, int32_t *ids
 int flint_moe_route(const uint16_t *x, const uint16_t *router, int M, int H, int E,
                     int top_k, uint16_t *logits, int32_t *ids, float *tw,
                     void *ws, size_t ws_bytes, void *stream);
+
+/* Wait errors of the decode calls that used workspace ws: queues on
+ * `stream` a copy of the workspace's wait-error word (an OR of FLINT_WAIT_*
+ * bits, 0 = every wait ended normally) into *errors, a device int32, and
+ * clears the word.  Read *errors after synchronising the stream. */
+int flint_moe_wait_errors(void *ws, size_t ws_bytes, int32_t *errors, void *stream);
 
 /* The MoE block on NVFP4 experts for decode-size batches, 1 <= M <= 64
  * (page "vllm.models.flint.ops.moe", flint_moe, decode branch):

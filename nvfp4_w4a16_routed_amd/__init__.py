@@ -29,7 +29,7 @@ STATUS = {0: "FLINT_OK", -1: "FLINT_ERR_NULL", -2: "FLINT_ERR_SHAPE", -3: "FLINT
 EXPORTS = ("flint_status_str", "flint_last_hip_error", "flint_moe_workspace_bytes",
            "flint_moe_workspace_init", "flint_nvfp4_dequant", "flint_moe_topk",
            "flint_moe_route", "flint_moe_decode", "flint_moe_grouped",
-           "flint_moe_bf16_decode", "flint_moe_ll")
+           "flint_moe_bf16_decode", "flint_moe_ll", "flint_moe_wait_errors")
 
 
 class FlintError(RuntimeError):
@@ -65,7 +65,13 @@ STAGES = ("route", "pair_lists", "shared_gate_up", "gate_up", "down", "shared_do
 class MoeDebug(ctypes.Structure):
     _fields_ = [("ids_in", P), ("tw_in", P), ("logits_out", P), ("ids_out", P),
                 ("tw_out", P), ("act_out", P), ("y_out", P), ("sact_out", P),
-                ("sh_out", P), ("stage_events", ctypes.POINTER(P))]
+                ("sh_out", P), ("stage_events", ctypes.POINTER(P)), ("wait_polls", I32),
+                ("wait_probe", I32)]
+
+
+# Bits of the word flint_moe_wait_errors returns (include/flint_moe.h).
+WAIT_KINDS = {1: "logits", 2: "shared_gate_up", 4: "gate_up", 8: "combine_shared",
+              16: "combine_down", 32: "lds", 64: "probe"}
 
 
 _lib = None
@@ -100,6 +106,8 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.restype = I32
             fn.argtypes = moe_args
+        L.flint_moe_wait_errors.restype = I32
+        L.flint_moe_wait_errors.argtypes = [P, ctypes.c_size_t, P, P]
         L.flint_moe_ll.restype = I32
         L.flint_moe_ll.argtypes = [P, P, P, ctypes.c_float, P, P, P, I32, I32, I32, I32, I32, P, P, P,
                                    P, P, ctypes.c_size_t, P]
@@ -152,6 +160,17 @@ def make_workspace(max_M: int, H: int, E: int, I: int, SI: int, top_k: int,
     return ws
 
 
+def flint_moe_wait_errors(ws, errors=None, stream=None) -> torch.Tensor:
+    """Queues a copy of the workspace's wait-error word into `errors` (a
+    device int32 tensor of one element, allocated when None) and clears the
+    word; returns `errors` (read it after synchronising)."""
+    errors = torch.zeros(1, dtype=torch.int32, device=ws.device) if errors is None else errors
+    _check("flint_moe_wait_errors",
+           lib().flint_moe_wait_errors(_ptr(ws), ws.numel() * ws.element_size(), _ptr(errors),
+                                       _stream(stream)))
+    return errors
+
+
 def flint_nvfp4_dequant(w: torch.Tensor, s: torch.Tensor, out: torch.Tensor | None = None,
                         stream=None) -> torch.Tensor:
     rows, K = w.shape[0], w.shape[1] * 2
@@ -202,13 +221,15 @@ def _shared_struct(shared):
 
 
 def _debug_struct(debug):
-    """debug: dict of tensors named after MoeDebug's fields; "stage_events" may
-    hold a ctypes array of FLINT_STAGE_EVENTS hipEvent_t handles."""
+    """debug: dict of tensors named after MoeDebug's pointer fields;
+    "stage_events" may hold a ctypes array of FLINT_STAGE_EVENTS hipEvent_t
+    handles; "wait_polls" and "wait_probe" are ints (test hooks)."""
     if not debug:
         return None
-    vals = [_ptr(debug.get(f)) for f, _ in MoeDebug._fields_[:-1]]
+    vals = [_ptr(debug.get(f)) for f, _ in MoeDebug._fields_[:9]]
     ev = debug.get("stage_events")
-    return MoeDebug(*vals, ctypes.cast(ev, ctypes.POINTER(P)) if ev is not None else None)
+    return MoeDebug(*vals, ctypes.cast(ev, ctypes.POINTER(P)) if ev is not None else None,
+                    int(debug.get("wait_polls", 0)), int(debug.get("wait_probe", 0)))
 
 
 def _moe_call(name, wstruct, x, router, shared, I, E, top_k, ws, out, debug, stream):

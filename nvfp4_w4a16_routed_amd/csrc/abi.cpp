@@ -140,6 +140,8 @@ int run_decode(int fmt, const uint16_t *x, const uint16_t *router, const void *w
   a.out = out;
   a.sync = W.sync;
   a.seq = next_seq();
+  a.polls = dbg ? dbg->wait_polls : 0;
+  a.probe = dbg ? dbg->wait_probe : 0;
   a.M = M;
   a.H = H;
   a.E = E;
@@ -189,6 +191,15 @@ int flint_moe_workspace_init(void *ws, size_t ws_bytes, void *stream) {
   if (!aligned16(ws)) return FLINT_ERR_ALIGN;
   if (ws_bytes < kCounterBytes) return FLINT_ERR_WORKSPACE;
   return hip_status(hipMemsetAsync(ws, 0, ws_bytes, (hipStream_t)stream));
+}
+
+int flint_moe_wait_errors(void *ws, size_t ws_bytes, int32_t *errors, void *stream) {
+  if (!errors) return FLINT_ERR_NULL;
+  if (!ws) return FLINT_ERR_WORKSPACE;
+  if (!aligned16(ws) || (reinterpret_cast<uintptr_t>(errors) & 3u)) return FLINT_ERR_ALIGN;
+  if (ws_bytes < sizeof(DecodeSync)) return FLINT_ERR_WORKSPACE;
+  return hip_status(launch_take_wait_errors(static_cast<DecodeSync *>(ws), errors,
+                                            (hipStream_t)stream));
 }
 
 int flint_nvfp4_dequant(const uint8_t *w, const uint8_t *s, int rows, int K, uint16_t *out,
@@ -312,8 +323,14 @@ int flint_moe_grouped(const uint16_t *x, const uint16_t *router, const flint_nvf
   const bool has_shared = !ext_sh && shared && shared->w_gu;
   const int SI = has_shared ? shared->SI : 0;
   if (M < 0 || top_k < 1 || E < 1 || top_k > E || E > kMaxExperts) return FLINT_ERR_SHAPE;
-  if ((long)M * top_k > (long)1 << 30) return FLINT_ERR_SHAPE;
   if (!grouped_shape_supported(H, I, SI)) return FLINT_ERR_SHAPE;
+  if (has_shared && SI < 64) return FLINT_ERR_SHAPE;  // a shared expert has a width
+  // x, act and sact are read through buffer descriptors (byte offsets below
+  // 2^31)
+  const long long kDesc = 1ll << 31;
+  if ((long long)M * H * 2 >= kDesc || (long long)M * top_k * I * 2 >= kDesc ||
+      (long long)M * SI * 2 >= kDesc)
+    return FLINT_ERR_SHAPE;
   if (M == 0) return FLINT_OK;  // nothing to compute; no pointer is used
   if (!x || !w || !out || (!forced && !router)) return FLINT_ERR_NULL;
   if (!w->w13 || !w->s13 || !w->a13 || !w->w2 || !w->s2 || !w->a2) return FLINT_ERR_NULL;

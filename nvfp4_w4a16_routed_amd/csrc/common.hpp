@@ -136,8 +136,8 @@ __device__ __forceinline__ int wave_max_i32(int v) {
 // ("agent") relaxed atomic accesses: such stores are performed at the
 // device's coherence point and such loads read from it, so no L2 writeback
 // or invalidate is needed.  A producer publishes by waiting until its
-// stores are performed (s_waitcnt vmcnt(0)) and then incrementing an arrival
-// counter; a consumer polls the counter and then reads the data.
+// stores are performed (s_waitcnt vmcnt(0)) and then writing a flag word; a
+// consumer polls the flag and then reads the data.
 
 template <typename T>
 __device__ __forceinline__ void st_dev(T *p, T v) {
@@ -154,35 +154,11 @@ __device__ __forceinline__ u32x4_t ld_dev16(const void *p) {
   return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
 }
 
-__device__ __forceinline__ int atomic_add_agent(int *p, int v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int load_agent(const int *p) { return ld_dev(p); }
-__device__ __forceinline__ void store_agent(int *p, int v) { st_dev(p, v); }
 
 // Waits until every store this wave issued has been performed.
 __device__ __forceinline__ void stores_performed() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // keeps the compiler's order
   __builtin_amdgcn_s_waitcnt(0x0F70);                     // vmcnt(0) (expcnt, lgkmcnt: any)
-}
-
-// Spins until *p >= target, backing off briefly between polls.  The
-// producers are running blocks that never wait on the caller, so the wait
-// ends; as a guard against a workspace whose counters were not zero, it
-// gives up after about 2^22 polls (seconds) so the kernel still ends.
-__device__ __forceinline__ bool wait_at_least(const int *p, int target) {
-  int naps = 1;
-  bool ok = false;
-  for (int it = 0; it < (1 << 22); ++it) {
-    if (load_agent(p) >= target) {
-      ok = true;
-      break;
-    }
-    for (int i = 0; i < naps; ++i) __builtin_amdgcn_s_sleep(2);
-    naps = naps < 4 ? naps * 2 : 4;
-  }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");  // keeps the compiler's order
-  return ok;
 }
 
 // ------------------------------------------------------------ memory ops

@@ -3,7 +3,7 @@
 // Semantics (vLLM page "vllm.models.flint.ops.moe": module docstring
 // "Numerics"; _router_kernel/_topk_row, _gate_up_gemv_kernel,
 // _down_gemv_kernel, their BF16 variants and _combine_kernel):
-//   logits = bf16(fp32 x . router[e]);  top-k by the order-preserving key
+//   logits = bf16(fp32 x . router[e]);  top-k: larger logit, then smaller index
 //   s_j = RN32(1 / RN32(1 + RN32(exp(-l_j)))), tw_j = bf16(s_j / (S + 1e-20))
 //   g, u = fp32 (x . W13[e, n]) * alpha13[e], (x . W13[e, I+n]) * alpha13[e]
 //   act = bf16(silu(g) * u);  y = bf16(fp32 (act . W2[e, h]) * alpha2[e])
@@ -46,6 +46,9 @@
 #include "common.hpp"
 #include "internal.hpp"
 #include "rowdot.hpp"
+#include "topk.hpp"
+
+#include <mutex>
 
 namespace flint {
 
@@ -63,6 +66,17 @@ constexpr int kCachePolicyDevice = 16;
 // Register budget: at least this many waves per SIMD (one 16-wave block per
 // CU), so enough weight bytes are in flight per CU.
 constexpr int kWavesPerEU = 4;
+
+// Kinds of bounded waits, recorded in DecodeSync::wait_err when one gives up.
+enum WaitKind {
+  kWaitLogits = 1,          // a token's tagged router logits
+  kWaitSharedGateUp = 2,    // the shared gate/up blocks' flags
+  kWaitGateUp = 4,          // the gate/up blocks of a routed expert
+  kWaitCombineShared = 8,   // the shared down blocks of a combine item
+  kWaitCombineDown = 16,    // the routed down blocks of a combine item
+  kWaitLds = 32,            // a wave of the same block (LDS counter)
+  kWaitProbe = 64           // the test hook's wait
+};
 
 struct Params {
   const uint16_t *x;
@@ -88,6 +102,8 @@ struct Params {
   uint16_t *out;
   DecodeSync *sync;
   int seq;
+  int polls;          // polls before a device-scope wait gives up
+  int probe;          // non-zero: block 0 also waits for a word nobody sets
   int M, E, top_k;
   int nb;             // blocks in the grid
   int n_route;        // routing items (0 with forced routing)
@@ -156,31 +172,34 @@ __device__ __forceinline__ void set_flag(int *f, int seq) {
   if (lane_id() == 0) st_dev(f, seq);
 }
 
+// A wait that gave up records its kind in the workspace's error word (one
+// device-scope OR per wave): the call's results are then not valid, and the
+// host reads the word with flint_moe_wait_errors.
+__device__ __forceinline__ void wait_failed(DecodeSync *S, int kind) {
+  if (lane_id() == 0)
+    __hip_atomic_fetch_or(&S->wait_err, kind, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // One wave polls until flags[i] == seq for every i in [lo, hi) (all lanes
-// read in parallel); gives up after a bounded number of polls.
-__device__ void wave_wait_flags(const int *flags, int lo, int hi, int seq) {
-  for (int it = 0, nap = 1; it < (1 << 20); ++it) {
+// read in parallel); after `polls` polls it gives up and records `kind`.
+__device__ void wave_wait_flags(const int *flags, int lo, int hi, int seq, int polls,
+                                DecodeSync *S, int kind) {
+  bool done = false;
+  for (int it = 0, nap = 1; it < polls; ++it) {
     bool ok = true;
     for (int i = lo + lane_id(); i < hi; i += kWave) ok &= ld_dev(&flags[i]) == seq;
-    if (__all(ok)) break;
+    if (__all(ok)) {
+      done = true;
+      break;
+    }
     for (int s = 0; s < nap; ++s) __builtin_amdgcn_s_sleep(2);
     nap = nap < 4 ? nap * 2 : 4;
   }
+  if (!done) wait_failed(S, kind);
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");  // keeps the compiler's order
 }
 
 // ---------------------------------------------------------------- top-k
-
-__device__ __forceinline__ int topk_key(uint32_t bits, int e, int E) {
-  int b = (int)(bits & 0xffffu);
-  int ord = (b >= 0x8000) ? (b ^ 0xffff) : (b | 0x8000);
-  return (ord << 8) | (E - 1 - e);
-}
-
-__device__ __forceinline__ uint32_t key_bits(int key) {
-  int o = key >> 8;
-  return (uint32_t)((o >= 0x8000) ? (o ^ 0x8000) : (o ^ 0xffff));
-}
 
 // The block's routing of the call (LDS).
 struct Route {
@@ -241,16 +260,17 @@ __device__ __forceinline__ int owner(const Route &R, const int *cum, int s, int 
 
 // Top-k of token t by one wave (top_k <= E <= 256) into LDS.  The logits
 // are polled until every one carries this call's sequence number (bounded:
-// after ~2^20 polls it goes on with what it read, so the kernel still
-// ends).  Block 0 also writes the plain bf16 logits.  The token's selected
+// after P.polls polls it records the failure and goes on with what it read,
+// so the kernel still ends).  Block 0 also writes the plain bf16 logits.  The token's selected
 // experts are also OR-ed into R.tokmask.
 //
-// Selection: the keys (the logit's order-preserving image, then the
-// reversed expert index) are unique, so the top_k largest are exactly those
-// >= the top_k-th largest key, found bit by bit from the top with ballot
-// counts.  The selected keys are then ranked among themselves (descending
-// key = the pages' selection order), which fixes the order of ids, of the
-// weights and of the fp32 sum of the scores.
+// Selection: the keys (rank_key: the logit's order, then the smaller expert
+// index) are unique, so the top_k largest are exactly those >= the top_k-th
+// largest key.  A small top_k takes top_k rounds of a wave maximum; a larger
+// one finds the threshold key by a radix search with ballot counts, and the
+// selected keys are then ranked among themselves (descending key = the
+// selection order), which fixes the order of ids, of the weights and of the
+// fp32 sum of the scores.
 __device__ void topk_token(const Params &P, int t, Route &R, int *scratch) {
   const int lane = lane_id();
   const int E = P.E, k = P.top_k;
@@ -266,22 +286,27 @@ __device__ void topk_token(const Params &P, int t, Route &R, int *scratch) {
     ee[i] = valid[i] ? ee[i] : E - 1;
   }
   unsigned long long v[4];
-  for (int it = 0, nap = 1; it < (1 << 20); ++it) {
+  bool done = false;
+  for (int it = 0, nap = 1; it < P.polls; ++it) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = ld_dev(&trow[ee[i]]);
     bool ok = true;
 #pragma unroll
     for (int i = 0; i < 4; ++i) ok &= !valid[i] || (uint32_t)(v[i] >> 32) == (uint32_t)P.seq;
-    if (__all(ok)) break;
+    if (__all(ok)) {
+      done = true;
+      break;
+    }
     for (int z = 0; z < nap; ++z) __builtin_amdgcn_s_sleep(2);
     nap = nap < 8 ? nap * 2 : 8;
   }
+  if (!done) wait_failed(P.sync, kWaitLogits);
   TRACE(P, 13);
   int keys[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t bits = (uint32_t)v[i] & 0xffffu;
-    keys[i] = valid[i] ? topk_key(bits, ee[i], E) : -1;
+    keys[i] = valid[i] ? rank_key(bits, ee[i]) : kNoKey;
   }
   if (blockIdx.x == 0) {
 #pragma unroll
@@ -290,32 +315,35 @@ __device__ void topk_token(const Params &P, int t, Route &R, int *scratch) {
   }
   // Lanes j < top_k (top_k <= 64 here) get the selected keys, lane j the
   // (j+1)-th largest (0 = largest = first in the pages' order).
-  int key = -1;
+  int key = kNoKey;
   if (k <= kTopkByMax) {
     // k rounds of a wave maximum (keys are unique): the short dependent
     // chain of a small top_k
     for (int r = 0; r < k; ++r) {
       const int m = wave_max_i32(max(max(keys[0], keys[1]), max(keys[2], keys[3])));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) keys[i] = keys[i] == m ? -1 : keys[i];
+      for (int i = 0; i < 4; ++i) keys[i] = keys[i] == m ? kNoKey : keys[i];
       key = lane == r ? m : key;
     }
   } else {
-    // the top_k-th largest key (keys are 24-bit, non-negative when valid),
-    // bit by bit from the top with ballot counts
+    // the top_k-th largest key, by a radix search from the top bit with
+    // ballot counts over the keys offset to [0, 2^24) (no key: -1)
+    int ukey[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ukey[i] = keys[i] == kNoKey ? -1 : keys[i] + (1 << 23);
     int thr = 0;
 #pragma unroll
     for (int bit = 23; bit >= 0; --bit) {
       const int cand = thr | (1 << bit);
-      const int cnt = __popcll(__ballot(keys[0] >= cand)) + __popcll(__ballot(keys[1] >= cand)) +
-                      __popcll(__ballot(keys[2] >= cand)) + __popcll(__ballot(keys[3] >= cand));
+      const int cnt = __popcll(__ballot(ukey[0] >= cand)) + __popcll(__ballot(ukey[1] >= cand)) +
+                      __popcll(__ballot(ukey[2] >= cand)) + __popcll(__ballot(ukey[3] >= cand));
       thr = cnt >= k ? cand : thr;
     }
     // compact the selected keys into scratch[0 .. k), then rank them
     int base = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool sel = keys[i] >= thr;
+      const bool sel = ukey[i] >= thr;
       const unsigned long long m = __ballot(sel);
       if (sel) scratch[base + __popcll(m & ((1ull << lane) - 1ull))] = keys[i];
       base += __popcll(m);
@@ -323,27 +351,21 @@ __device__ void topk_token(const Params &P, int t, Route &R, int *scratch) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int ck = lane < k ? scratch[lane] : -1;
+    const int ck = lane < k ? scratch[lane] : kNoKey;
     int rank = 0;
     for (int j = 0; j < k; ++j) rank += __builtin_amdgcn_readlane(ck, j) > ck;
     // lane rank takes key ck
     key = __builtin_amdgcn_ds_permute(rank * 4, ck);
-    key = lane < k ? key : -1;
+    key = lane < k ? key : kNoKey;
   }
-  float sc = 0.0f;
-  if (lane < k) {
-    const float l = bf16_to_f32(key_bits(key));
-    const float a = (float)exp(-(double)l);  // correctly rounded for every bf16 l
-    const float d = 1.0f + a;
-    sc = 1.0f / d;
-  }
+  const float sc = lane < k ? router_score(key) : 0.0f;
   // the fp32 sum of the scores in selection order, one addition at a time
   float S = 0.0f;
   for (int r = 0; r < k; ++r)
     S = S + __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc), r));
   const float D = S + 1e-20f;
   if (lane < k) {
-    const int e = E - 1 - (key & 0xff);
+    const int e = key_expert(key);
     R.ids[t * k + lane] = e;
     R.tw[t * k + lane] = round_bf16(sc / D);
     atomicOr(&R.tokmask[e], 1ull << t);
@@ -356,7 +378,8 @@ __device__ void topk_token_long(const Params &P, int t, Route &R) {
   const int E = P.E, k = P.top_k;
   const unsigned long long *trow = P.tlog + (size_t)t * E;
   unsigned long long v[4] = {0ull, 0ull, 0ull, 0ull};
-  for (int it = 0, nap = 1; it < (1 << 20); ++it) {
+  bool done = false;
+  for (int it = 0, nap = 1; it < P.polls; ++it) {
     bool ok = true;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -366,37 +389,33 @@ __device__ void topk_token_long(const Params &P, int t, Route &R) {
         ok &= (uint32_t)(v[i] >> 32) == (uint32_t)P.seq;
       }
     }
-    if (__all(ok)) break;
+    if (__all(ok)) {
+      done = true;
+      break;
+    }
     for (int z = 0; z < nap; ++z) __builtin_amdgcn_s_sleep(2);
     nap = nap < 8 ? nap * 2 : 8;
   }
-  int keys[4], sel[4] = {-1, -1, -1, -1};
+  if (!done) wait_failed(P.sync, kWaitLogits);
+  int keys[4], sel[4] = {kNoKey, kNoKey, kNoKey, kNoKey};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + kWave * i;
     const uint32_t bits = (uint32_t)v[i] & 0xffffu;
-    keys[i] = (e < E) ? topk_key(bits, e, E) : -1;
+    keys[i] = (e < E) ? rank_key(bits, e) : kNoKey;
     if (blockIdx.x == 0 && e < E) P.logits[(size_t)t * E + e] = (uint16_t)bits;
   }
   for (int j = 0; j < k; ++j) {
     int best = wave_max_i32(max(max(keys[0], keys[1]), max(keys[2], keys[3])));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (keys[i] == best) keys[i] = -1;
+      if (keys[i] == best) keys[i] = kNoKey;
       if ((j >> 6) == i && lane == (j & (kWave - 1))) sel[i] = best;
     }
   }
   float s[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    s[i] = 0.0f;
-    if (kWave * i + lane < k) {
-      const float l = bf16_to_f32(key_bits(sel[i]));
-      const float a = (float)exp(-(double)l);
-      const float d = 1.0f + a;
-      s[i] = 1.0f / d;
-    }
-  }
+  for (int i = 0; i < 4; ++i) s[i] = kWave * i + lane < k ? router_score(sel[i]) : 0.0f;
   float S = 0.0f;
   for (int j = 0; j < k; ++j) {
     const int i = j >> 6;
@@ -408,7 +427,7 @@ __device__ void topk_token_long(const Params &P, int t, Route &R) {
   for (int i = 0; i < 4; ++i) {
     const int j = kWave * i + lane;
     if (j < k) {
-      const int e = E - 1 - (sel[i] & 0xff);
+      const int e = key_expert(sel[i]);
       R.ids[t * k + j] = e;
       R.tw[t * k + j] = round_bf16(s[i] / D);
       atomicOr(&R.tokmask[e], 1ull << t);
@@ -487,22 +506,25 @@ __device__ void build_plan_wave(const Params &P, Route &R) {
   if (lane == 0) __hip_atomic_store(&R.plan_ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// Waits (bounded) until an LDS counter of the block reaches n.
-__device__ __forceinline__ void wait_lds_at_least(int *c, int n) {
+// Waits until an LDS counter of the block reaches n.  The waves it waits for
+// belong to the same (resident) block and their own waits are bounded, so
+// this ends; as a guard it gives up after 2^22 polls and records kWaitLds.
+__device__ __forceinline__ void wait_lds_at_least(int *c, int n, DecodeSync *S) {
+  bool done = false;
   for (int it = 0; it < (1 << 22); ++it) {
-    if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= n) break;
+    if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= n) {
+      done = true;
+      break;
+    }
     __builtin_amdgcn_s_sleep(1);
   }
+  if (!done) wait_failed(S, kWaitLds);
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-// Waits (LDS, bounded) until the block's plan is built.
-__device__ __forceinline__ void wait_plan(Route &R) {
-  for (int it = 0; it < (1 << 22); ++it) {
-    if (__hip_atomic_load(&R.plan_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0) break;
-    __builtin_amdgcn_s_sleep(1);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+// Waits until the block's plan is built (as wait_lds_at_least).
+__device__ __forceinline__ void wait_plan(Route &R, DecodeSync *S) {
+  wait_lds_at_least(&R.plan_ready, 1, S);
 }
 
 // --------------------------------------------------------- phase A items
@@ -747,6 +769,10 @@ decode_kernel(Params P) {
   }
   if (threadIdx.x < kMaxExperts) R.tokmask[threadIdx.x] = 0ull;
   __syncthreads();  // publishes the counters
+  // Test hook: one wave waits for a word that no block ever sets, so the
+  // wait gives up and records kWaitProbe (the host asks for it).
+  if (P.probe && blockIdx.x == 0 && wv == 0)
+    wave_wait_flags(&S->probe, 0, 1, ~P.seq, P.polls, S, kWaitProbe);
 
   // ---- phase A1: routing items, one per wave from the last wave of each
   // block down (item r: block r % nb); they read x from global memory.
@@ -763,7 +789,7 @@ decode_kernel(Params P) {
     if (lane == 0) atomicAdd(&R.x_staged, 1);
   }
   auto wait_x = [&]() {
-    if (x_all) wait_lds_at_least(&R.x_staged, kWaves - 1);
+    if (x_all) wait_lds_at_least(&R.x_staged, kWaves - 1, S);
   };
 
   // Shared-expert items go to every block: shared gate/up items to its
@@ -822,10 +848,10 @@ decode_kernel(Params P) {
         // the block's first shared down wave polls the flags, the others
         // wait for its word in LDS
         if (ws == 0) {
-          wave_wait_flags(S->sg, sh0, sh0 + min(nbs, P.n_sgu), P.seq);
+          wave_wait_flags(S->sg, sh0, sh0 + min(nbs, P.n_sgu), P.seq, P.polls, S, kWaitSharedGateUp);
           if (lane == 0) __hip_atomic_store(&R.sg_ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         } else {
-          wait_lds_at_least(&R.sg_ready, 1);
+          wait_lds_at_least(&R.sg_ready, 1, S);
         }
         waited = true;
       }
@@ -884,7 +910,7 @@ decode_kernel(Params P) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       build_plan_wave<Gm::N_GU, Gm::N_DN>(P, R);
     } else {
-      wait_plan(R);
+      wait_plan(R, S);
     }
     __builtin_amdgcn_s_setprio(0);
   }
@@ -998,8 +1024,9 @@ decode_kernel(Params P) {
       if (s != cur) {
         cur = s;
         wave_wait_flags(S->gb, owner_block(R, R.cum_gu, s, 0, QB, P.nb),
-                        owner_block(R, R.cum_gu, s, Gm::N_GU - 1, QB, P.nb) + 1, P.seq);
-        if (nx > 0) wait_lds_at_least(&R.done_b, kWaves);
+                        owner_block(R, R.cum_gu, s, Gm::N_GU - 1, QB, P.nb) + 1, P.seq, P.polls, S,
+                        kWaitGateUp);
+        if (nx > 0) wait_lds_at_least(&R.done_b, kWaves, S);
         for (int j = 0; j < nc + nx; ++j)  // every row's copies in flight at once
           issue_copy_to_lds<true>(j < nc ? slice + (size_t)j * I : xpart + (size_t)(j - nc) * I,
                                   P.act + (size_t)pr[j] * I, I / 8, 0, 1);
@@ -1043,17 +1070,24 @@ decode_kernel(Params P) {
     // before comparing any (one round trip): a chunk's items lie in at most
     // two blocks' shares when a share holds IPB items or more (the blocks
     // between the two ends are read one by one otherwise).
-    if (P.sgu)
-      for (int it = 0, nap = 1; it < (1 << 20); ++it) {
+    if (P.sgu) {
+      bool done = false;
+      for (int it = 0, nap = 1; it < P.polls; ++it) {
         bool ok = true;
         for (int j = h0 / Gm::SDN::RW + lane; j < (h0 + Gm::CB) / Gm::SDN::RW; j += kWave)
           ok &= ld_dev(&S->sd[sh0 + j % nbs]) == P.seq;
-        if (__all(ok)) break;
+        if (__all(ok)) {
+          done = true;
+          break;
+        }
         for (int z = 0; z < nap; ++z) __builtin_amdgcn_s_sleep(2);
         nap = nap < 4 ? nap * 2 : 4;
       }
+      if (!done) wait_failed(S, kWaitCombineShared);
+    }
     constexpr int IPB = Gm::CB / Gm::DN::RW;  // down items per combine item
-    for (int it = 0, nap = 1; it < (1 << 20); ++it) {
+    bool cdone = false;
+    for (int it = 0, nap = 1; it < P.polls; ++it) {
       bool ok = true;
       for (int s0 = 0; s0 < U; s0 += kWave) {
         const int s = s0 + lane < U ? s0 + lane : U - 1;
@@ -1064,10 +1098,14 @@ decode_kernel(Params P) {
         ok &= f0 == P.seq && f1 == P.seq;
         for (int b = b_lo + 1; b < b_hi; ++b) ok &= ld_dev(&S->db[b]) == P.seq;
       }
-      if (__all(ok)) break;
+      if (__all(ok)) {
+        cdone = true;
+        break;
+      }
       for (int z = 0; z < nap; ++z) __builtin_amdgcn_s_sleep(2);
       nap = nap < 4 ? nap * 2 : 4;
     }
+    if (!cdone) wait_failed(S, kWaitCombineDown);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     // y of the rows for a group of tokens is gathered into this wave's LDS
     // slice with direct loads (one round trip per group), then summed.
@@ -1150,6 +1188,36 @@ struct GridInfo {
   int nb = 0;
 };
 
+// Decode launches are chained per device: every block of the grid must be
+// resident at once (the blocks wait on each other), so two decode grids on
+// different streams must not run together.  Each launch is followed by an
+// event record; a launch on a stream other than the previous launch's first
+// waits for that event.  Launches on one stream are ordered by the stream.
+struct LaunchChain {
+  std::mutex mu;
+  hipEvent_t done = nullptr;
+  hipStream_t last = nullptr;
+  bool any = false;
+};
+LaunchChain g_chain[64];  // [device]
+
+template <typename F>
+hipError_t chained_launch(int dev, hipStream_t st, F &&launch_fn) {
+  LaunchChain &c = g_chain[dev];
+  std::lock_guard<std::mutex> lock(c.mu);
+  hipError_t e;
+  if (!c.done && (e = hipEventCreateWithFlags(&c.done, hipEventDisableTiming)) != hipSuccess) {
+    c.done = nullptr;
+    return e;
+  }
+  if (c.any && c.last != st && (e = hipStreamWaitEvent(st, c.done, 0)) != hipSuccess) return e;
+  if ((e = launch_fn()) != hipSuccess) return e;
+  if ((e = hipEventRecord(c.done, st)) != hipSuccess) return e;
+  c.last = st;
+  c.any = true;
+  return hipSuccess;
+}
+
 template <int FMT, int H, int I>
 hipError_t launch(Params P, hipStream_t st) {
   using Gm = Geo<FMT, H, I>;
@@ -1180,11 +1248,23 @@ hipError_t launch(Params P, hipStream_t st) {
   P.n_sgu = P.sgu ? I / Gm::SGU::RP : 0;  // shared gate/up items (row pairs)
   P.n_sdn = P.sgu ? H / Gm::SDN::RW : 0;  // shared down items
   if (P.nb > kMaxSharedBlocks) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_kernel<FMT, H, I>), dim3(P.nb), dim3(kThreads), lds, st, P);
-  return hipGetLastError();
+  return chained_launch(dev, st, [&]() {
+    hipLaunchKernelGGL((decode_kernel<FMT, H, I>), dim3(P.nb), dim3(kThreads), lds, st, P);
+    return hipGetLastError();
+  });
+}
+
+__global__ void take_wait_errors_kernel(DecodeSync *sync, int32_t *out) {
+  *out = sync->wait_err;
+  sync->wait_err = 0;
 }
 
 }  // namespace
+
+hipError_t launch_take_wait_errors(DecodeSync *sync, int32_t *out, hipStream_t st) {
+  hipLaunchKernelGGL(take_wait_errors_kernel, dim3(1), dim3(1), 0, st, sync, out);
+  return hipGetLastError();
+}
 
 #ifdef FLINT_TRACE
 long long *g_flint_trace = nullptr;
@@ -1215,6 +1295,8 @@ hipError_t launch_decode(int fmt, const DecodeArgs &a, hipStream_t st) {
   P.out = a.out;
   P.sync = a.sync;
   P.seq = a.seq;
+  P.polls = a.polls > 0 ? a.polls : (1 << 20);
+  P.probe = a.probe;
   P.M = a.M;
   P.E = a.E;
   P.top_k = a.top_k;

@@ -865,7 +865,7 @@ hipError_t side_stream(int dev, SideStream **out) {
 
 bool grouped_shape_supported(int H, int I, int SI) {
   return H % 128 == 0 && I % 64 == 0 && H >= 128 && I >= 64 && H <= 8192 && I <= 8192 &&
-         (SI == 0 || (SI % 64 == 0 && SI <= 8192));
+         (SI == 0 || (SI % 64 == 0 && SI >= 64 && SI <= 8192));
 }
 
 hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {

@@ -29,6 +29,8 @@ struct DecodeSync {
   int sd[kMaxSharedBlocks];  // shared down block done
   int gb[kMaxDecodeBlocks];  // the block's routed gate/up items done
   int db[kMaxDecodeBlocks];  // the block's routed down items done
+  int wait_err;              // OR of the kinds of waits that gave up (0 = none)
+  int probe;                 // never written: the target of the test hook's wait
 };
 
 // The route kernel's arrival counters follow the decode block: token groups
@@ -53,7 +55,9 @@ struct DecodeArgs {
   float *tw;
   uint16_t *act, *y, *sact, *sh, *out;
   DecodeSync *sync;
-  int seq;  // call sequence number (never 0; unique per call)
+  int seq;    // call sequence number (never 0; unique per call)
+  int polls;  // polls before a device-scope wait gives up (0 = default)
+  int probe;  // test hook: non-zero makes one wait give up
   int M, H, E, I, top_k;
 };
 
@@ -115,6 +119,9 @@ hipError_t launch_decode(int fmt, const DecodeArgs &a, hipStream_t st);
 
 // Whether the decode kernel is compiled for this (H, I) (both formats).
 bool decode_shape_supported(int H, int I);
+
+// Queues: *out = sync->wait_err, then sync->wait_err = 0.
+hipError_t launch_take_wait_errors(DecodeSync *sync, int32_t *out, hipStream_t st);
 
 // Arguments of the grouped (prefill) path: device pointers, caller-owned.
 struct GroupedArgs {

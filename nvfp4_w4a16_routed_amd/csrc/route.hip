@@ -5,9 +5,9 @@
 // "Numerics", the router kernel _router_kernel and the top-k routine
 // _topk_row):
 //   logits[t, e] = bf16(fp32 sum_h x[t, h] * router[e, h])
-//   selection: keys (order-preserving 16-bit image of the logit bits) << 8 |
-//              (E - 1 - e); k rounds of "take the largest key" (ties go to
-//              the lowest expert index), E <= 256
+//   selection: the larger logit first, equal logits by the smaller expert
+//              index (rank_key in topk.hpp); k rounds of "take the largest
+//              remaining key", E <= 256
 //   s_j  = RN32(1 / RN32(1 + RN32(exp(-l_j))))  (exact exp, RN division)
 //   tw_j = bf16(RN32(s_j / RN32(S + 1e-20))), S = fp32 sum of the s_j in
 //          selection order.
@@ -20,6 +20,7 @@
 // works and the workspace is clean after every call.
 #include "common.hpp"
 #include "internal.hpp"
+#include "topk.hpp"
 
 namespace flint {
 
@@ -27,53 +28,31 @@ namespace {
 
 constexpr int kThreads = 256;  // 4 waves
 
-// Order-preserving integer image of bf16 bits, widened with the expert
-// index so every key is unique: larger key = larger logit, then lower index.
-__device__ __forceinline__ int topk_key(uint32_t bits, int e, int E) {
-  int b = (int)(bits & 0xffffu);
-  int ord = (b >= 0x8000) ? (b ^ 0xffff) : (b | 0x8000);
-  return (ord << 8) | (E - 1 - e);
-}
-
-// Inverse of the key's logit part: key >> 8 back to bf16 bits.
-__device__ __forceinline__ uint32_t key_bits(int key) {
-  int o = key >> 8;
-  return (uint32_t)((o >= 0x8000) ? (o ^ 0x8000) : (o ^ 0xffff));
-}
-
 // Top-k of one token's logits by one wave (top_k <= E <= 256).  Selection j
 // is kept in a register of lane j % 64 (slot j / 64).  Writes the ids, tw
 // and (if non-NULL) scores rows of the token.
 __device__ void topk_token(const uint16_t *lrow, int E, int top_k, int32_t *ids, float *tw,
                            float *scores) {
   const int lane = threadIdx.x & (kWave - 1);
-  int keys[4], sel[4] = {-1, -1, -1, -1};
+  int keys[4], sel[4] = {kNoKey, kNoKey, kNoKey, kNoKey};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     int e = lane + kWave * i;
-    keys[i] = (e < E) ? topk_key(lrow[e], e, E) : -1;
+    keys[i] = (e < E) ? rank_key(lrow[e], e) : kNoKey;
   }
   for (int j = 0; j < top_k; ++j) {
     int m = max(max(keys[0], keys[1]), max(keys[2], keys[3]));
     int best = wave_max_i32(m);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (keys[i] == best) keys[i] = -1;
+      if (keys[i] == best) keys[i] = kNoKey;
       if ((j >> 6) == i && lane == (j & (kWave - 1))) sel[i] = best;
     }
   }
   // Sigmoid score of each selected logit, by the lane that holds it.
   float s[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    s[i] = 0.0f;
-    if (kWave * i + lane < top_k) {
-      float l = bf16_to_f32(key_bits(sel[i]));
-      float a = (float)exp(-(double)l);  // correctly rounded for every bf16 l
-      float d = 1.0f + a;
-      s[i] = 1.0f / d;
-    }
-  }
+  for (int i = 0; i < 4; ++i) s[i] = kWave * i + lane < top_k ? router_score(sel[i]) : 0.0f;
   // Renormalisation: fp32 sum in selection order, then one RN division each.
   float S = 0.0f;
   for (int j = 0; j < top_k; ++j) {
@@ -86,7 +65,7 @@ __device__ void topk_token(const uint16_t *lrow, int E, int top_k, int32_t *ids,
   for (int i = 0; i < 4; ++i) {
     const int j = kWave * i + lane;
     if (j < top_k) {
-      ids[j] = E - 1 - (sel[i] & 0xff);
+      ids[j] = key_expert(sel[i]);
       tw[j] = round_bf16(s[i] / D);
       if (scores) scores[j] = s[i];
     }

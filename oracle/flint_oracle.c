@@ -85,8 +85,9 @@ double orc_e4m3fn(unsigned b) {
 }
 
 /* Packed codes: byte c of a row holds K elements 2c (low nibble) and 2c+1
- * (high nibble).  The pages unpack one int32 word into its eight codes "in
- * natural order"; with little-endian words that is this nibble order. */
+ * (high nibble).  The pages unpack each int32 word into its eight codes in
+ * ascending K order (page "vllm.models.flint.ops.moe", _dequant_rows); with
+ * little-endian words that is this nibble order (reading S2). */
 static unsigned nibble(const uint8_t *row, long k) {
   uint8_t b = row[k >> 1];
   return (k & 1) ? (unsigned)(b >> 4) : (unsigned)(b & 15u);
@@ -151,12 +152,39 @@ float orc_router_score(uint16_t logit_bits) {
   return 1.0f / d;
 }
 
-/* Top-k of one row of bf16 logits, after the top-k routine on the page
- * "vllm.models.flint.ops.moe" (_topk_row): each logit's bits are mapped to an
- * order-preserving 16-bit integer (negative values: all bits flipped;
- * non-negative values: sign bit set), shifted left by 8 and combined with
- * E-1-e, so the largest key is the largest logit and, among equal logits,
- * the lowest expert index.  k selections of the largest remaining key.
+/* Whether logit a (bf16 bits) of expert ia ranks above logit b of expert ib
+ * in the routing selection.  The rule (page "vllm.models.flint.ops.moe",
+ * "Numerics" paragraph and the top-k routine _topk_row of the router): the
+ * larger logit comes first and equal logits go to the smaller expert index.
+ * Points the rule leaves to the bit patterns (reading S12):
+ *   - +0 ranks above -0;
+ *   - a NaN whose sign bit is clear ranks above +inf, one whose sign bit is
+ *     set below -inf; among NaNs of one sign the larger payload lies further
+ *     from zero (above for the positive sign, below for the negative).
+ * Written here as comparisons of values and classes, not as an integer key. */
+static int ranks_above(uint16_t a, long ia, uint16_t b, long ib) {
+  const float fa = orc_bf16_to_f32(a), fb = orc_bf16_to_f32(b);
+  const int na = isnan(fa), nb = isnan(fb);
+  /* class: 2 = positive NaN, 1 = a number (finite or infinite), 0 = negative NaN */
+  const int ca = na ? (signbit(fa) ? 0 : 2) : 1;
+  const int cb = nb ? (signbit(fb) ? 0 : 2) : 1;
+  if (ca != cb) return ca > cb;
+  if (ca == 1) {
+    if (fa != fb) return fa > fb;
+    if (!signbit(fa) != !signbit(fb)) return signbit(fb) != 0; /* +0 above -0 */
+    return ia < ib;
+  }
+  /* two NaNs of one sign: by payload, away from zero */
+  const int pa = a & 0x7f, pb = b & 0x7f;
+  if (pa != pb) return ca == 2 ? pa > pb : pa < pb;
+  return ia < ib;
+}
+
+/* Top-k of one row of bf16 logits with renormalised sigmoid weights (page
+ * "vllm.models.flint.ops.moe", the "Numerics" paragraph and _topk_row).
+ * Each expert's place in the descending order is the number of experts that
+ * rank above it (ranks_above); those at places 0 .. k-1 are selected, and
+ * place j is ids[t, j].
  *
  * Scores s_j (fp32) of the selected logits are renormalised:
  *   S = s_0 + s_1 + ... + s_{k-1}   (fp32, left to right in selection order;
@@ -167,25 +195,19 @@ float orc_router_score(uint16_t logit_bits) {
  * scores (may be NULL) receives s_j. */
 void orc_topk(const uint16_t *logits, long M, long E, long k, int32_t *ids,
               float *tw, float *scores) {
+#pragma omp parallel for schedule(static)
   for (long t = 0; t < M; ++t) {
     const uint16_t *row = logits + t * E;
-    int32_t *keys = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
-    for (long e = 0; e < E; ++e) {
-      int32_t bits = row[e];
-      int32_t ord = (bits >= 0x8000) ? (bits ^ 0xFFFF) : (bits | 0x8000);
-      keys[e] = (ord << 8) | (int32_t)(E - 1 - e);
-    }
     float s[256];
-    for (long j = 0; j < k; ++j) {
-      long best = 0;
-      for (long e = 1; e < E; ++e)
-        if (keys[e] > keys[best]) best = e;
-      /* best is the index of the largest key; its low byte is E-1-best */
-      ids[t * k + j] = (int32_t)best;
-      s[j] = orc_router_score(row[best]);
-      keys[best] = -1;
+    for (long e = 0; e < E; ++e) {
+      long place = 0;
+      for (long f = 0; f < E; ++f)
+        if (f != e && ranks_above(row[f], f, row[e], e)) ++place;
+      if (place < k) {
+        ids[t * k + place] = (int32_t)e;
+        s[place] = orc_router_score(row[e]);
+      }
     }
-    free(keys);
     float S = 0.0f;
     for (long j = 0; j < k; ++j) S = S + s[j];
     float D = S + 1e-20f;

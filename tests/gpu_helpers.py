@@ -195,23 +195,92 @@ def same_f32(a, b) -> bool:
         a[~np.isnan(a)].view(np.uint32), b[~np.isnan(b)].view(np.uint32))
 
 
-def stagewise(inp, r, say=print):
+def error_report(out_gpu, ref: dict, k: int, rows=None) -> dict:
+    """Plain error figures of out against the oracle's out over `rows`
+    (tokens routed identically): max absolute error, max relative error
+    (|err| / |ref| over nonzero ref), and the histogram of |err| in units of
+    ulp_bf16(out_ref) (0, 1, 2, >2)."""
+    M = ref["out"].shape[0]
+    rows = np.ones(M, bool) if rows is None else np.asarray(rows, bool)
+    r = bf(ref["out"])[rows]
+    g = bf(np.asarray(out_gpu))[rows]
+    err = np.abs(g - r)
+    nz = r != 0
+    u = err / ulp_bf16(r)
+    hist = {"0": int(np.sum(u == 0)), "1": int(np.sum((u > 0) & (u <= 1))),
+            "2": int(np.sum((u > 1) & (u <= 2))), ">2": int(np.sum(u > 2))}
+    return dict(max_abs=float(err.max()) if err.size else 0.0,
+                max_rel=float(np.max(err[nz] / np.abs(r[nz]))) if np.any(nz) else 0.0,
+                ulp_out_hist=hist, elements=int(err.size))
+
+
+def record(entry: dict) -> None:
+    """Appends one JSON line to the file named by $FLINT_PARITY_REPORT (if set)."""
+    import json
+    import os
+    path = os.environ.get("FLINT_PARITY_REPORT")
+    if path:
+        with open(path, "a") as fh:
+            fh.write(json.dumps(entry) + "\n")
+
+
+def stagewise_routing(inp, r):
+    """Logits within tolerance; ids / tw bit-exact given the GPU's logits."""
+    cfg = inp["cfg"]
+    ref_lg = oracle.logits(inp["x"], inp["router"])
+    check_logits(r["logits"], ref_lg, inp["x"], inp["router"], cfg["name"])
+    rids, rtw, _ = oracle.topk(r["logits"], cfg["top_k"])
+    assert np.array_equal(r["ids"], rids), "ids differ from the oracle's top-k of the GPU's logits"
+    assert same_f32(r["tw"], rtw), "tw differ from the oracle's top-k of the GPU's logits"
+
+
+def stagewise_routed(inp, r):
+    """Routed act on the GPU's routing and y on the GPU's act."""
+    cfg = inp["cfg"]
+    k, I, H, label = cfg["top_k"], cfg["I"], cfg["H"], cfg["name"]
+    act, det = oracle.gate_up(inp["x"], r["ids"], k, inp, I, want_detail=True)
+    check_act(r["act"], act, det, label)
+    y, ydet = oracle.down(r["act"], r["ids"], inp, H, want_detail=True)
+    check_y(r["y"], y, ydet, label)
+
+
+def end_to_end(inp, r, say=print, sh_in=None, extra=None):
+    """The GPU's out against the oracle's own routing (tokens routed
+    identically), within 2 ulp of m; prints and records the error figures.
+    sh_in: a precomputed shared output that replaces the oracle's shared
+    expert."""
+    cfg = inp["cfg"]
+    k, label = cfg["top_k"], cfg["name"]
+    full = oracle.moe_block(inp)
+    if sh_in is not None:
+        full = dict(full)
+        full["sh"] = sh_in
+        full["out"], full["routed"] = oracle.combine(full["y"], full["tw"], sh_in, k)
+    same = np.all(full["ids"] == r["ids"], axis=1)
+    ulps = end_to_end_ulps(r["out"], full, k, rows=same)
+    rep = error_report(r["out"], full, k, rows=same)
+    say(f"{label}: tokens {cfg['M']}, near-tie flips {int((~same).sum())}, "
+        f"max ulp(m) {ulps.max() if ulps.size else 0:.3f}, "
+        f"mean nonzero {np.mean(ulps > 0) if ulps.size else 0:.4f}, "
+        f"max abs {rep['max_abs']:.3g}, max rel {rep['max_rel']:.3g}, "
+        f"ulp(out_ref) histogram {rep['ulp_out_hist']}")
+    entry = dict(workload=label, M=cfg["M"], E=cfg["E"], top_k=k, H=cfg["H"], I=cfg["I"],
+                 near_tie_flips=int((~same).sum()),
+                 max_ulp_m=float(ulps.max()) if ulps.size else 0.0, **rep)
+    entry.update(extra or {})
+    record(entry)
+    assert ulps.size == 0 or ulps.max() <= 2.0
+    return full
+
+
+def stagewise(inp, r, say=print, extra=None):
     """Checks every stage of a GPU run against the oracle fed with the GPU's
     own upstream values; returns the oracle's end-to-end result."""
     cfg = inp["cfg"]
-    k, I, H = cfg["top_k"], cfg["I"], cfg["H"]
+    k, H = cfg["top_k"], cfg["H"]
     label = cfg["name"]
-    # routing: ids / tw bit-exact given the GPU's logits
-    ref_lg = oracle.logits(inp["x"], inp["router"])
-    check_logits(r["logits"], ref_lg, inp["x"], inp["router"], label)
-    rids, rtw, _ = oracle.topk(r["logits"], k)
-    assert np.array_equal(r["ids"], rids) and same_f32(r["tw"], rtw)
-    # gate/up on the GPU's routing
-    act, det = oracle.gate_up(inp["x"], r["ids"], k, inp, I, want_detail=True)
-    check_act(r["act"], act, det, label)
-    # down on the GPU's act
-    y, ydet = oracle.down(r["act"], r["ids"], inp, H, want_detail=True)
-    check_y(r["y"], y, ydet, label)
+    stagewise_routing(inp, r)
+    stagewise_routed(inp, r)
     sh = None
     if "sgu" in inp:
         sact, sh_ref, sdet = oracle.shared_expert(inp["x"], inp["sgu"], inp["sdown"], True)
@@ -223,14 +292,4 @@ def stagewise(inp, r, say=print):
     # combine: bit-exact on the GPU's y, tw and shared output
     out_c, _ = oracle.combine(r["y"], r["tw"], sh, k)
     assert np.array_equal(r["out"], out_c), "combine differs"
-    # end to end against the oracle's own routing
-    full = oracle.moe_block(inp)
-    same = np.all(full["ids"] == r["ids"], axis=1)
-    ulps = end_to_end_ulps(r["out"], full, k, rows=same)
-    say(f"{label}: tokens {cfg['M']}, near-tie flips {int((~same).sum())}, "
-         f"max ulp(m) {ulps.max() if ulps.size else 0:.3f}, "
-         f"mean nonzero {np.mean(ulps > 0) if ulps.size else 0:.4f}")
-    assert ulps.size == 0 or ulps.max() <= 2.0
-    return full
-
-
+    return end_to_end(inp, r, say, extra=extra)

@@ -121,6 +121,41 @@ def test_bf16_decode_and_grouped_reject_bad_arguments():
                                    1 << 30, None) == -3
 
 
+def _grouped(M=8, H=2048, E=128, I=768, k=8, shared=None, ws_bytes=1 << 62):
+    w = _experts()
+    return fm.lib().flint_moe_grouped(A, A, ctypes.byref(w), ctypes.byref(shared) if shared else None,
+                                      M, H, E, I, k, A, None, A, ws_bytes, None)
+
+
+def test_grouped_rejects_sizes_past_its_addressing():
+    # x, act and sact are read through 32-bit buffer offsets: each must stay
+    # below 2^31 bytes (act = M * top_k * I * 2 bytes reaches it first)
+    assert _grouped(M=174762, k=8, I=768, ws_bytes=10) == -4   # 2^31 - 2^20-ish: accepted sizes
+    assert _grouped(M=174763, k=8, I=768) == -2                # act past 2^31 bytes
+    assert _grouped(M=(1 << 30) // 2048, H=2048, k=1, I=64) == -2  # x = 2^31 bytes
+    assert _grouped(M=(1 << 30) // 2048 - 1, H=2048, k=1, I=64, ws_bytes=10) == -4
+    sh = fm.SharedExpert(A, A, 8192)
+    assert _grouped(M=(1 << 30) // 8192, H=128, k=1, I=64, shared=sh) == -2  # sact = 2^31 bytes
+
+
+def test_grouped_rejects_bad_shared_widths():
+    assert _grouped(shared=fm.SharedExpert(A, A, 0)) == -2     # a shared expert of width 0
+    assert _grouped(shared=fm.SharedExpert(A, A, -64)) == -2
+    assert _grouped(shared=fm.SharedExpert(A, A, 96)) == -2    # not a multiple of 64
+    assert _grouped(shared=fm.SharedExpert(A, A, 8256)) == -2
+    assert _grouped(shared=fm.SharedExpert(A, None, 768)) == -1
+    assert _grouped(shared=fm.SharedExpert(A, A, 768), ws_bytes=10) == -4  # the sizes pass
+    assert _grouped(M=0) == 0
+
+
+def test_wait_errors_rejects_bad_arguments():
+    L = fm.lib()
+    assert L.flint_moe_wait_errors(A, 1 << 20, None, None) == -1
+    assert L.flint_moe_wait_errors(None, 1 << 20, A, None) == -4
+    assert L.flint_moe_wait_errors(A, 16, A, None) == -4
+    assert L.flint_moe_wait_errors(MIS, 1 << 20, A, None) == -3
+
+
 def test_topk_route_dequant_reject_bad_arguments():
     L = fm.lib()
     assert L.flint_moe_topk(A, 4, 300, 8, A, A, None, None) == -2

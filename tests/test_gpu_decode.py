@@ -147,6 +147,22 @@ def test_decode_small_stagewise(M, E, k, H, I, SI):
     G.stagewise(inp, r)
 
 
+@pytest.mark.parametrize("M,E,k,H,I,SI", [
+    (2, 256, 16, 256, 128, 128),   # the largest top_k taken by rounds of a wave maximum
+    (4, 256, 24, 256, 128, 128),   # threshold (radix) search
+    (8, 256, 64, 256, 128, 0),     # threshold search, top_k = one wave
+    (4, 256, 128, 256, 128, 128),  # top_k beyond a wave: rounds over four slots per lane
+    (2, 256, 256, 256, 128, 0),    # every expert selected, top_k = E = 256
+    (3, 100, 65, 512, 128, 128),   # E not a multiple of the wave, top_k just past it
+])
+def test_decode_large_topk_stagewise(M, E, k, H, I, SI):
+    """The decode kernel's top-k branches beyond top_k = 16."""
+    _say(f"decode large top_k M={M} E={E} k={k} H={H} I={I} SI={SI}")
+    inp = synth.make_small(250 + M + k, M=M, H=H, E=E, I=I, SI=SI, top_k=k, router_std=0.3)
+    r = G.run_block(fm, inp, "decode")
+    G.stagewise(inp, r, _say)
+
+
 @pytest.mark.parametrize("M,E,k,H,I,SI", [(4, 8, 2, 256, 128, 128), (9, 16, 4, 512, 256, 256)])
 def test_bf16_decode_small_stagewise(M, E, k, H, I, SI):
     _say(f"bf16 decode small M={M} E={E} k={k} H={H} I={I}")
@@ -163,7 +179,7 @@ def test_decode_full_size_configs(cfg):
     inp = synth.make_inputs(cfg)
     path = "bf16_decode" if c["experts"] == "bf16" else "decode"
     r = G.run_block(fm, inp, path)
-    G.stagewise(inp, r)
+    G.stagewise(inp, r, _say, extra=dict(path=path, config=cfg))
 
 
 def test_forced_routing_and_determinism():

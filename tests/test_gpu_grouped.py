@@ -41,6 +41,8 @@ def _say(*a):
     (300, 16, 4, 512, 256, 192),     # experts with > 64 rows, 3 shared column tiles
     (700, 4, 4, 256, 128, 64),       # every expert > 256 rows: several row tiles each
     (129, 32, 8, 2048, 768, 768),    # the real H and I
+    (300, 256, 8, 256, 128, 128),    # E = 256: the router's second 128-expert slab
+    (70, 200, 12, 256, 128, 0),      # a partial second slab, no shared expert
 ])
 def test_grouped_small_stagewise(M, E, k, H, I, SI):
     _say(f"grouped M={M} E={E} k={k} H={H} I={I} SI={SI}")
@@ -130,7 +132,12 @@ def test_grouped_full_prefill_sampled():
     G.check_logits(lg[sample], ref["logits"], inp["x"][sample], inp["router"], "prefill")
     same = np.all(ref["ids"] == ids[sample], axis=1)
     ulps = G.end_to_end_ulps(G.host(out)[sample], ref, k, rows=same)
+    rep = G.error_report(G.host(out)[sample], ref, k, rows=same)
     _say(f"  sampled tokens {len(sample)}, near-tie flips {int((~same).sum())}, "
-         f"max ulp(m) {ulps.max():.3f}")
+         f"max ulp(m) {ulps.max():.3f}, max abs {rep['max_abs']:.3g}, max rel {rep['max_rel']:.3g}, "
+         f"ulp(out_ref) histogram {rep['ulp_out_hist']}")
+    G.record(dict(workload=cfg["name"], M=M, E=E, top_k=k, H=H, I=I, path="grouped", config=4,
+                  sampled_tokens=len(sample), near_tie_flips=int((~same).sum()),
+                  max_ulp_m=float(ulps.max()), **rep))
     assert ulps.max() <= 2.0
     assert (~same).sum() <= 2

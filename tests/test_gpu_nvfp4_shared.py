@@ -38,11 +38,17 @@ def test_grouped_nvfp4_shared_expert(M, H, SI):
     shd = {kk: G.dev(v) for kk, v in shw.items()}
     ws = fm.make_workspace(M, H, E, I, SI, k)
     z = lambda shape, dt: torch.empty(shape, dtype=dt, device="cuda")
-    dbg = dict(ids_out=z((M, k), torch.int32), tw_out=z((M, k), torch.float32),
+    dbg = dict(logits_out=z((M, E), torch.int16), ids_out=z((M, k), torch.int32),
+               tw_out=z((M, k), torch.float32), act_out=z((M * k, I), torch.int16),
                y_out=z((M * k, H), torch.int16), sact_out=z((M, SI), torch.int16),
                sh_out=z((M, H), torch.int16))
     out = fm.flint_moe_grouped(d["x"], d["router"], G.experts_of(d), shd, k, ws, debug=dbg)
     torch.cuda.synchronize()
+    r = {kk[:-4]: G.host(v) for kk, v in dbg.items()}
+    r["out"] = G.host(out)
+    # the routed experts at these shapes, as in the other parity tests
+    G.stagewise_routing(inp, r)
+    G.stagewise_routed(inp, r)
     one = np.zeros((M, 1), dtype=np.int32)
     sact = G.host(dbg["sact_out"]).view(np.uint16)
     ref_sact, det = oracle.gate_up(inp["x"], one, 1, shw, SI, want_detail=True)
@@ -52,3 +58,15 @@ def test_grouped_nvfp4_shared_expert(M, H, SI):
     G.check_y(sh, ref_sh, det2, "nvfp4 shared down")
     out_c, _ = oracle.combine(G.host(dbg["y_out"]).view(np.uint16), G.host(dbg["tw_out"]), sh, k)
     assert np.array_equal(G.host(out).view(np.uint16), out_c)
+    # end to end: the oracle's block with the NVFP4 shared expert's output
+    # (its own gate/up and down with one expert every token selects)
+    full = oracle.moe_block(inp)
+    ref_sact_own = oracle.gate_up(inp["x"], one, 1, shw, SI)
+    ref_sh_own = oracle.down(ref_sact_own, one, shw, H)
+    full["sh"] = ref_sh_own
+    full["out"], full["routed"] = oracle.combine(full["y"], full["tw"], ref_sh_own, k)
+    same = np.all(full["ids"] == r["ids"], axis=1)
+    ulps = G.end_to_end_ulps(r["out"], full, k, rows=same)
+    assert ulps.size == 0 or ulps.max() <= 2.0
+    print(f"  near-tie flips {int((~same).sum())}, max ulp(m) {ulps.max() if ulps.size else 0:.3f}",
+          flush=True)

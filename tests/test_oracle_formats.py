@@ -178,6 +178,26 @@ def test_topk_special_values():
     assert sc[0, 0] == 1.0  # sigmoid(+inf)
 
 
+def test_topk_any_bit_pattern_matches_sign_magnitude_sort():
+    """Every bf16 bit pattern, NaNs and signed zeros included, against a brute
+    force sort on the sign-magnitude integer of the bits (negative patterns
+    below every non-negative one, ordered by decreasing magnitude; -0 just
+    below +0), ties to the lower index: the total order the pages' selection
+    key induces, stated without that key."""
+    rng = np.random.default_rng(11)
+    for E in (5, 64, 256):
+        lg = rng.integers(0, 1 << 16, size=(30, E)).astype(np.uint16)
+        lg[:, : E // 3] = lg[:, [0]]  # repeated patterns: ties
+        for k in sorted({1, min(E, 4), E}):
+            ids, tw, sc = oracle.topk(lg, k)
+            for t in range(lg.shape[0]):
+                def sm(b):
+                    b = int(b)
+                    return (b & 0x7FFF) if b < 0x8000 else -(b & 0x7FFF) - 1
+                order = sorted(range(E), key=lambda e: (-sm(lg[t, e]), e))[:k]
+                assert list(ids[t]) == order
+
+
 def test_routing_weights_closed_forms():
     # all logits equal: s_j equal, tw = RNb(1/k) exactly representable for k=2^n
     for k in (1, 2, 4, 8):
