@@ -48,6 +48,8 @@
 #include "rowdot.hpp"
 #include "topk.hpp"
 
+#include <hip/hip_ext.h>
+
 #include <mutex>
 
 namespace flint {
@@ -1190,9 +1192,11 @@ struct GridInfo {
 
 // Decode launches are chained per device: every block of the grid must be
 // resident at once (the blocks wait on each other), so two decode grids on
-// different streams must not run together.  Each launch is followed by an
-// event record; a launch on a stream other than the previous launch's first
-// waits for that event.  Launches on one stream are ordered by the stream.
+// different streams must not run together.  Each launch carries a stop
+// event in its own dispatch (hipExtLaunchKernel: no separate marker between
+// back-to-back launches); a launch on a stream other than the previous
+// launch's first waits for that event.  Launches on one stream are ordered
+// by the stream.
 struct LaunchChain {
   std::mutex mu;
   hipEvent_t done = nullptr;
@@ -1201,18 +1205,18 @@ struct LaunchChain {
 };
 LaunchChain g_chain[64];  // [device]
 
+// launch_fn(stop_event) queues the kernel with the given stop event.
 template <typename F>
 hipError_t chained_launch(int dev, hipStream_t st, F &&launch_fn) {
   LaunchChain &c = g_chain[dev];
   std::lock_guard<std::mutex> lock(c.mu);
   hipError_t e;
-  if (!c.done && (e = hipEventCreateWithFlags(&c.done, hipEventDisableTiming)) != hipSuccess) {
+  if (!c.done && (e = hipEventCreate(&c.done)) != hipSuccess) {
     c.done = nullptr;
     return e;
   }
   if (c.any && c.last != st && (e = hipStreamWaitEvent(st, c.done, 0)) != hipSuccess) return e;
-  if ((e = launch_fn()) != hipSuccess) return e;
-  if ((e = hipEventRecord(c.done, st)) != hipSuccess) return e;
+  if ((e = launch_fn(c.done)) != hipSuccess) return e;
   c.last = st;
   c.any = true;
   return hipSuccess;
@@ -1248,9 +1252,10 @@ hipError_t launch(Params P, hipStream_t st) {
   P.n_sgu = P.sgu ? I / Gm::SGU::RP : 0;  // shared gate/up items (row pairs)
   P.n_sdn = P.sgu ? H / Gm::SDN::RW : 0;  // shared down items
   if (P.nb > kMaxSharedBlocks) return hipErrorInvalidValue;
-  return chained_launch(dev, st, [&]() {
-    hipLaunchKernelGGL((decode_kernel<FMT, H, I>), dim3(P.nb), dim3(kThreads), lds, st, P);
-    return hipGetLastError();
+  return chained_launch(dev, st, [&](hipEvent_t stop) {
+    void *args[] = {&P};
+    return hipExtLaunchKernel(reinterpret_cast<const void *>(&decode_kernel<FMT, H, I>), dim3(P.nb),
+                              dim3(kThreads), args, lds, st, nullptr, stop, 0);
   });
 }
 
