@@ -203,7 +203,9 @@ int flint_moe_route(const uint16_t *x, const uint16_t *router, int M, int H, int
 /* Wait errors of the decode calls that used workspace ws: queues on
  * `stream` a copy of the workspace's wait-error word (an OR of FLINT_WAIT_*
  * bits, 0 = every wait ended normally) into *errors, a device int32, and
- * clears the word.  Read *errors after synchronising the stream. */
+ * clears the word.  Read *errors after synchronising the stream.  ws = NULL
+ * reads the library's own scratch on the current device (the calls of
+ * flint_moe_decode_noalloc); ws_bytes is then ignored. */
 int flint_moe_wait_errors(void *ws, size_t ws_bytes, int32_t *errors, void *stream);
 
 /* The MoE block on NVFP4 experts for decode-size batches, 1 <= M <= 64
@@ -214,6 +216,24 @@ int flint_moe_decode(const uint16_t *x, const uint16_t *router,
                      int M, int H, int E, int I, int top_k, uint16_t *out,
                      const flint_moe_debug *dbg, void *ws, size_t ws_bytes,
                      void *stream);
+
+/* flint_moe_decode without a workspace, for callers that cannot allocate
+ * device memory (serving loops that must not call hipMalloc, harnesses that
+ * forbid it).  Same arguments (minus ws), rule, limits and errors as
+ * flint_moe_decode; no memory is allocated or freed.  Its scratch is a
+ * 4 MiB array inside the library, one per GPU, kept until the process
+ * ends; sizes whose workspace would exceed it (flint_moe_workspace_bytes)
+ * return FLINT_ERR_WORKSPACE (every size the decode entry points accept
+ * fits).  Every call on a GPU shares that GPU's scratch: calls are ordered
+ * by the library's per-device launch chain, but two calls must not be
+ * queued concurrently from different host threads with debug outputs that
+ * alias.  Nothing in the scratch needs clearing between calls (its flags
+ * hold per-call sequence numbers).  Sequence numbers are taken when the call
+ * is queued, so a graph that captured the call must not be replayed. */
+int flint_moe_decode_noalloc(const uint16_t *x, const uint16_t *router,
+                             const flint_nvfp4_experts *w, const flint_shared_expert *shared,
+                             int M, int H, int E, int I, int top_k, uint16_t *out,
+                             const flint_moe_debug *dbg, void *stream);
 
 /* The decode MoE block behind a residual add and RMS norm (page
  * "vllm.models.flint.ops.moe", flint_moe_ll with _add_rms_norm):

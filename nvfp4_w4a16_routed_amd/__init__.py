@@ -29,7 +29,8 @@ STATUS = {0: "FLINT_OK", -1: "FLINT_ERR_NULL", -2: "FLINT_ERR_SHAPE", -3: "FLINT
 EXPORTS = ("flint_status_str", "flint_last_hip_error", "flint_moe_workspace_bytes",
            "flint_moe_workspace_init", "flint_nvfp4_dequant", "flint_moe_topk",
            "flint_moe_route", "flint_moe_decode", "flint_moe_grouped",
-           "flint_moe_bf16_decode", "flint_moe_ll", "flint_moe_wait_errors")
+           "flint_moe_bf16_decode", "flint_moe_ll", "flint_moe_wait_errors",
+           "flint_moe_decode_noalloc")
 
 
 class FlintError(RuntimeError):
@@ -106,6 +107,8 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.restype = I32
             fn.argtypes = moe_args
+        L.flint_moe_decode_noalloc.restype = I32
+        L.flint_moe_decode_noalloc.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, P, P, P]
         L.flint_moe_wait_errors.restype = I32
         L.flint_moe_wait_errors.argtypes = [P, ctypes.c_size_t, P, P]
         L.flint_moe_ll.restype = I32
@@ -163,11 +166,14 @@ def make_workspace(max_M: int, H: int, E: int, I: int, SI: int, top_k: int,
 def flint_moe_wait_errors(ws, errors=None, stream=None) -> torch.Tensor:
     """Queues a copy of the workspace's wait-error word into `errors` (a
     device int32 tensor of one element, allocated when None) and clears the
-    word; returns `errors` (read it after synchronising)."""
-    errors = torch.zeros(1, dtype=torch.int32, device=ws.device) if errors is None else errors
+    word; returns `errors` (read it after synchronising).  ws=None reads the
+    library's own scratch (flint_moe_decode_noalloc) on the current device."""
+    if errors is None:
+        errors = torch.zeros(1, dtype=torch.int32,
+                             device=ws.device if ws is not None else "cuda")
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check("flint_moe_wait_errors",
-           lib().flint_moe_wait_errors(_ptr(ws), ws.numel() * ws.element_size(), _ptr(errors),
-                                       _stream(stream)))
+           lib().flint_moe_wait_errors(_ptr(ws), nbytes, _ptr(errors), _stream(stream)))
     return errors
 
 
@@ -256,6 +262,24 @@ def flint_moe_decode(x, router, experts: dict, shared, top_k: int, ws, out=None,
     E, I = experts["w13"].shape[0], experts["w2"].shape[2] * 2
     st = nvfp4_experts_struct(*(experts[k] for k in ("w13", "s13", "a13", "w2", "s2", "a2")))
     return _moe_call("flint_moe_decode", st, x, router, shared, I, E, top_k, ws, out, debug, stream)
+
+
+def flint_moe_decode_noalloc(x, router, experts: dict, shared, top_k: int, out=None, debug=None,
+                             stream=None):
+    """flint_moe_decode on the library's own scratch (no workspace; the
+    library allocates nothing).  `out` must be given by callers that cannot
+    allocate (when None it is allocated here with torch)."""
+    E, I = experts["w13"].shape[0], experts["w2"].shape[2] * 2
+    M, H = x.shape
+    out = _new((M, H), x.dtype, x) if out is None else out
+    st = nvfp4_experts_struct(*(experts[k] for k in ("w13", "s13", "a13", "w2", "s2", "a2")))
+    sh = _shared_struct(shared)
+    dbg = _debug_struct(debug)
+    rc = lib().flint_moe_decode_noalloc(_ptr(x), _ptr(router), ctypes.byref(st),
+                                        ctypes.byref(sh) if sh else None, M, H, E, I, top_k, _ptr(out),
+                                        ctypes.byref(dbg) if dbg else None, _stream(stream))
+    _check("flint_moe_decode_noalloc", rc)
+    return out
 
 
 def flint_moe_ll(attn_out, residual, ln_weight, eps: float, router, experts: dict, shared, top_k: int,

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/flint_moe.h"
 #include "internal.hpp"
@@ -59,6 +60,39 @@ Workspace carve_workspace(void *base, int M, int H, int E, int I, int SI, int to
   w.sh_counts = static_cast<int32_t *>(take(16));
   w.bytes = off;
   return w;
+}
+
+// ---- The library's own scratch for flint_moe_decode_noalloc.
+//
+// A file-scope device array: each GPU the library runs on holds its own copy
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory, so its device address is looked up once per device with
+// hipGetSymbolAddress (with that device current) and only that address is
+// passed to kernels.  kScratchBytes covers the largest decode workspace the
+// decode entry points accept (M <= 64, M * top_k <= 512, E <= 256, H <= 2048,
+// I = SI <= 768: about 3.4 MiB).
+constexpr size_t kScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+static void *g_scratch_ptr[kMaxScratchDevices];
+static std::mutex g_scratch_mu;
+
+// The current device's address of `scratch` (looked up on first use).
+static hipError_t scratch_ptr(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace flint
@@ -195,7 +229,13 @@ int flint_moe_workspace_init(void *ws, size_t ws_bytes, void *stream) {
 
 int flint_moe_wait_errors(void *ws, size_t ws_bytes, int32_t *errors, void *stream) {
   if (!errors) return FLINT_ERR_NULL;
-  if (!ws) return FLINT_ERR_WORKSPACE;
+  if (!ws) {  // the library's own scratch (flint_moe_decode_noalloc)
+    if (reinterpret_cast<uintptr_t>(errors) & 3u) return FLINT_ERR_ALIGN;
+    void *p = nullptr;
+    if (hipError_t e = scratch_ptr(&p); e != hipSuccess) return hip_status(e);
+    return hip_status(launch_take_wait_errors(static_cast<DecodeSync *>(p), errors,
+                                              (hipStream_t)stream));
+  }
   if (!aligned16(ws) || (reinterpret_cast<uintptr_t>(errors) & 3u)) return FLINT_ERR_ALIGN;
   if (ws_bytes < sizeof(DecodeSync)) return FLINT_ERR_WORKSPACE;
   return hip_status(launch_take_wait_errors(static_cast<DecodeSync *>(ws), errors,
@@ -259,6 +299,33 @@ int flint_moe_decode(const uint16_t *x, const uint16_t *router, const flint_nvfp
     return FLINT_ERR_ALIGN;
   return run_decode(kNvfp4, x, router, w->w13, w->s13, w->a13, w->w2, w->s2, w->a2, shared, M,
                     H, E, I, top_k, out, dbg, ws, ws_bytes, (hipStream_t)stream);
+}
+
+int flint_moe_decode_noalloc(const uint16_t *x, const uint16_t *router,
+                             const flint_nvfp4_experts *w, const flint_shared_expert *shared,
+                             int M, int H, int E, int I, int top_k, uint16_t *out,
+                             const flint_moe_debug *dbg, void *stream) {
+  // Every argument check of flint_moe_decode, then the library's scratch in
+  // place of a caller workspace (too small for these sizes: FLINT_ERR_WORKSPACE).
+  const bool forced = dbg && dbg->ids_in;
+  int st = check_common(M, H, E, I, top_k);
+  if (st) return st;
+  if (M == 0) return FLINT_OK;
+  if (!x || !w || !out || (!forced && !router)) return FLINT_ERR_NULL;
+  if (!w->w13 || !w->s13 || !w->a13 || !w->w2 || !w->s2 || !w->a2) return FLINT_ERR_NULL;
+  if (forced && !dbg->tw_in) return FLINT_ERR_NULL;
+  if ((st = check_shared(shared, H, I))) return st;
+  if (!aligned16(x) || (router && !aligned16(router)) || !aligned16(out) || !aligned16(w->w13) ||
+      !aligned16(w->s13) || !aligned16(w->a13) || !aligned16(w->w2) || !aligned16(w->s2) ||
+      !aligned16(w->a2))
+    return FLINT_ERR_ALIGN;
+  const bool has_shared = shared && !shared->sh_in && shared->w_gu;
+  if (carve_workspace(nullptr, M, H, E, I, has_shared ? shared->SI : 0, top_k).bytes > kScratchBytes)
+    return FLINT_ERR_WORKSPACE;
+  void *ws = nullptr;
+  if (hipError_t e = scratch_ptr(&ws); e != hipSuccess) return hip_status(e);
+  return run_decode(kNvfp4, x, router, w->w13, w->s13, w->a13, w->w2, w->s2, w->a2, shared, M,
+                    H, E, I, top_k, out, dbg, ws, kScratchBytes, (hipStream_t)stream);
 }
 
 int flint_moe_ll(const uint16_t *attn_out, const uint16_t *residual, const uint16_t *ln_weight,

@@ -130,7 +130,7 @@ def _grouped(M=8, H=2048, E=128, I=768, k=8, shared=None, ws_bytes=1 << 62):
 def test_grouped_rejects_sizes_past_its_addressing():
     # x, act and sact are read through 32-bit buffer offsets: each must stay
     # below 2^31 bytes (act = M * top_k * I * 2 bytes reaches it first)
-    assert _grouped(M=174762, k=8, I=768, ws_bytes=10) == -4   # 2^31 - 2^20-ish: accepted sizes
+    assert _grouped(M=174762, k=8, I=768, ws_bytes=10) == -4   # act just below 2^31 bytes: accepted
     assert _grouped(M=174763, k=8, I=768) == -2                # act past 2^31 bytes
     assert _grouped(M=(1 << 30) // 2048, H=2048, k=1, I=64) == -2  # x = 2^31 bytes
     assert _grouped(M=(1 << 30) // 2048 - 1, H=2048, k=1, I=64, ws_bytes=10) == -4
@@ -151,7 +151,6 @@ def test_grouped_rejects_bad_shared_widths():
 def test_wait_errors_rejects_bad_arguments():
     L = fm.lib()
     assert L.flint_moe_wait_errors(A, 1 << 20, None, None) == -1
-    assert L.flint_moe_wait_errors(None, 1 << 20, A, None) == -4
     assert L.flint_moe_wait_errors(A, 16, A, None) == -4
     assert L.flint_moe_wait_errors(MIS, 1 << 20, A, None) == -3
 
@@ -171,3 +170,22 @@ def test_topk_route_dequant_reject_bad_arguments():
     assert L.flint_nvfp4_dequant(A, MIS, 4, 32, A, None) == -3
     assert L.flint_moe_workspace_init(None, 1 << 20, None) == -1
     assert L.flint_moe_workspace_init(A, 16, None) == -4
+
+
+def _noalloc(x=A, router=A, w=None, shared=None, M=8, H=2048, E=128, I=768, k=8, out=A, dbg=None):
+    w = _experts() if w is None else w
+    return fm.lib().flint_moe_decode_noalloc(x, router, ctypes.byref(w),
+                                             ctypes.byref(shared) if shared else None, M, H, E, I, k,
+                                             out, ctypes.byref(dbg) if dbg else None, None)
+
+
+def test_decode_noalloc_rejects_bad_arguments():
+    assert _noalloc(x=None) == -1
+    assert _noalloc(out=None) == -1
+    assert _noalloc(w=fm.NvFp4Experts(A, None, A, A, A, A)) == -1
+    assert _noalloc(M=65) == -2
+    assert _noalloc(k=200, E=256) == -2
+    assert _noalloc(H=1000) == -2
+    assert _noalloc(x=MIS) == -3
+    assert _noalloc(shared=fm.SharedExpert(A, A, 700)) == -2
+    assert _noalloc(M=0, x=None) == 0
