@@ -97,9 +97,10 @@ typedef struct {
  * shared_output / shared_ready): when sh_in != NULL the block computes no
  * shared expert (w_gu, w_down and SI are ignored) and adds sh_in [M, H]
  * bf16 (16-byte aligned) in its place, out = bf16(bf16(routed) + sh_in);
- * sh_ready, a hipEvent_t or NULL, is waited on by the call's stream just
- * before sh_in is read, so the producer may still be running when the call
- * is made. */
+ * sh_ready, a hipEvent_t or NULL, is waited on by the call's stream before
+ * sh_in is read (decode entry points: before the block's one kernel starts,
+ * whose combine reads it; flint_moe_grouped: before its combine kernel), so
+ * the producer may still be running when the call is made. */
 typedef struct {
   const uint16_t *w_gu;   /* [2*SI, H] bf16, rows 0..SI-1 gate, SI..2SI-1 up */
   const uint16_t *w_down; /* [H, SI] bf16 */
@@ -111,7 +112,9 @@ typedef struct {
    * E = 1, the same rule as the routed experts).  When s_gu != NULL, w_gu
    * holds E2M1 codes [2*SI, H/2] (bytes), s_gu [2*SI, H/16], a_gu -> the
    * device fp32 global scale, w_down codes [H, SI/2], s_down [H, SI/16],
-   * a_down.  Grouped path only: the decode entry points reject it. */
+   * a_down.  Accepted by flint_moe_grouped and by the NVFP4 decode entry
+   * points (flint_moe_decode, flint_moe_decode_noalloc, flint_moe_ll);
+   * flint_moe_bf16_decode rejects it (FLINT_ERR_SHAPE). */
   const uint8_t *s_gu, *s_down;
   const float *a_gu, *a_down;
 } flint_shared_expert;

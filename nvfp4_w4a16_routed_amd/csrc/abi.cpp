@@ -114,12 +114,19 @@ int check_common(int M, int H, int E, int I, int top_k) {
   return FLINT_OK;
 }
 
-int check_shared(const flint_shared_expert *sh, int H, int I) {
+// The decode entry points' shared expert: none, a precomputed output, a
+// bf16 expert, or (allow_nvfp4: NVFP4 routed experts) an NVFP4 expert.
+int check_shared(const flint_shared_expert *sh, int H, int I, bool allow_nvfp4) {
   if (sh && sh->sh_in) return aligned16(sh->sh_in) ? FLINT_OK : FLINT_ERR_ALIGN;
   if (!sh || !sh->w_gu) return FLINT_OK;
-  if (sh->s_gu) return FLINT_ERR_SHAPE;  // NVFP4 shared expert: grouped path only
+  if (sh->s_gu && !allow_nvfp4) return FLINT_ERR_SHAPE;
   if (!sh->w_down) return FLINT_ERR_NULL;
+  if (sh->s_gu && (!sh->s_down || !sh->a_gu || !sh->a_down)) return FLINT_ERR_NULL;
   if (!aligned16(sh->w_gu) || !aligned16(sh->w_down)) return FLINT_ERR_ALIGN;
+  if (sh->s_gu && (!aligned16(sh->s_gu) || !aligned16(sh->s_down) ||
+                   (reinterpret_cast<uintptr_t>(sh->a_gu) & 3u) ||
+                   (reinterpret_cast<uintptr_t>(sh->a_down) & 3u)))
+    return FLINT_ERR_ALIGN;
   if (!decode_shape_supported(H, sh->SI)) return FLINT_ERR_SHAPE;
   if (sh->SI != I) return FLINT_ERR_SHAPE;  // the decode kernel's shared expert is I wide
   return FLINT_OK;
@@ -161,6 +168,12 @@ int run_decode(int fmt, const uint16_t *x, const uint16_t *router, const void *w
   a.a2 = a2;
   a.sgu = has_shared ? reinterpret_cast<const uint8_t *>(shared->w_gu) : nullptr;
   a.sdown = has_shared ? reinterpret_cast<const uint8_t *>(shared->w_down) : nullptr;
+  const bool nv_sh = has_shared && shared->s_gu;
+  a.ssgu = nv_sh ? shared->s_gu : nullptr;
+  a.ssdown = nv_sh ? shared->s_down : nullptr;
+  a.asgu = nv_sh ? shared->a_gu : nullptr;
+  a.asdown = nv_sh ? shared->a_down : nullptr;
+  a.sh_ext = ext_sh ? shared->sh_in : nullptr;
   a.ids_in = forced ? dbg->ids_in : nullptr;
   a.tw_in = forced ? dbg->tw_in : nullptr;
   a.logits = logits;
@@ -181,14 +194,14 @@ int run_decode(int fmt, const uint16_t *x, const uint16_t *router, const void *w
   a.E = E;
   a.I = I;
   a.top_k = top_k;
+  // A precomputed shared output is read by the kernel's combine: the stream
+  // waits for its event before the launch (every block of the decode grid
+  // must be resident, so the kernel could not overlap its producer anyway).
+  hipError_t e = hipSuccess;
+  if (ext_sh && shared->sh_ready) e = hipStreamWaitEvent(st, (hipEvent_t)shared->sh_ready, 0);
   // One kernel runs every stage: the stage events bracket the whole of it.
-  hipError_t e = mark(0);
+  if (e == hipSuccess) e = mark(0);
   if (e == hipSuccess) e = launch_decode(fmt, a, st);
-  // Precomputed shared output: the kernel ran without a shared expert, so
-  // out holds bf16(routed) exactly; the rule's last step adds sh_in.
-  if (e == hipSuccess && ext_sh && shared->sh_ready)
-    e = hipStreamWaitEvent(st, (hipEvent_t)shared->sh_ready, 0);
-  if (e == hipSuccess && ext_sh) e = launch_add_bf16(out, shared->sh_in, (size_t)M * H, st);
   for (int i = 1; i < FLINT_STAGE_EVENTS && e == hipSuccess; ++i) e = mark(i);
   return hip_status(e);
 }
@@ -292,7 +305,7 @@ int flint_moe_decode(const uint16_t *x, const uint16_t *router, const flint_nvfp
   if (!w->w13 || !w->s13 || !w->a13 || !w->w2 || !w->s2 || !w->a2) return FLINT_ERR_NULL;
   if (forced && !dbg->tw_in) return FLINT_ERR_NULL;
   if (!ws) return FLINT_ERR_WORKSPACE;
-  if ((st = check_shared(shared, H, I))) return st;
+  if ((st = check_shared(shared, H, I, true))) return st;
   if (!aligned16(x) || (router && !aligned16(router)) || !aligned16(out) || !aligned16(ws) ||
       !aligned16(w->w13) || !aligned16(w->s13) || !aligned16(w->a13) || !aligned16(w->w2) ||
       !aligned16(w->s2) || !aligned16(w->a2))
@@ -314,7 +327,7 @@ int flint_moe_decode_noalloc(const uint16_t *x, const uint16_t *router,
   if (!x || !w || !out || (!forced && !router)) return FLINT_ERR_NULL;
   if (!w->w13 || !w->s13 || !w->a13 || !w->w2 || !w->s2 || !w->a2) return FLINT_ERR_NULL;
   if (forced && !dbg->tw_in) return FLINT_ERR_NULL;
-  if ((st = check_shared(shared, H, I))) return st;
+  if ((st = check_shared(shared, H, I, true))) return st;
   if (!aligned16(x) || (router && !aligned16(router)) || !aligned16(out) || !aligned16(w->w13) ||
       !aligned16(w->s13) || !aligned16(w->a13) || !aligned16(w->w2) || !aligned16(w->s2) ||
       !aligned16(w->a2))
@@ -347,7 +360,7 @@ int flint_moe_ll(const uint16_t *attn_out, const uint16_t *residual, const uint1
   if (!w->w13 || !w->s13 || !w->a13 || !w->w2 || !w->s2 || !w->a2) return FLINT_ERR_NULL;
   if (forced && !dbg->tw_in) return FLINT_ERR_NULL;
   if (!ws) return FLINT_ERR_WORKSPACE;
-  if ((st = check_shared(shared, H, I))) return st;
+  if ((st = check_shared(shared, H, I, true))) return st;
   if (carve_workspace(nullptr, M, H, E, I, shared && shared->w_gu ? shared->SI : 0, top_k).bytes > ws_bytes)
     return FLINT_ERR_WORKSPACE;
   if ((router && !aligned16(router)) || !aligned16(out) || !aligned16(ws) || !aligned16(w->w13) ||
@@ -373,7 +386,7 @@ int flint_moe_bf16_decode(const uint16_t *x, const uint16_t *router, const flint
   if (!w->w13 || !w->w2) return FLINT_ERR_NULL;
   if (forced && !dbg->tw_in) return FLINT_ERR_NULL;
   if (!ws) return FLINT_ERR_WORKSPACE;
-  if ((st = check_shared(shared, H, I))) return st;
+  if ((st = check_shared(shared, H, I, false))) return st;  // NVFP4 shared: NVFP4 experts only
   if (!aligned16(x) || (router && !aligned16(router)) || !aligned16(out) || !aligned16(ws) ||
       !aligned16(w->w13) || !aligned16(w->w2))
     return FLINT_ERR_ALIGN;

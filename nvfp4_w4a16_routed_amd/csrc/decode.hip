@@ -89,8 +89,11 @@ struct Params {
   const uint8_t *w2;
   const uint8_t *s2;
   const float *a2;
-  const uint8_t *sgu;    // shared [2I, H] bf16, NULL = no shared expert
-  const uint8_t *sdown;  // shared [H, I] bf16
+  const uint8_t *sgu;    // shared [2I, H] bf16 (or E2M1 codes), NULL = no shared expert
+  const uint8_t *sdown;  // shared [H, I] bf16 (or E2M1 codes)
+  const uint8_t *ssgu, *ssdown;  // NVFP4 shared expert: E4M3 block scales
+  const float *asgu, *asdown;    // NVFP4 shared expert: global scales (device)
+  const uint16_t *sh_ext;        // precomputed shared output [M, H], NULL = none
   const int32_t *ids_in; // forced routing (NULL = route)
   const float *tw_in;
   uint16_t *logits;
@@ -145,13 +148,13 @@ __shared__ long long g_trace_lds[kWaves * 16];
   } while (0)
 #endif
 
-// Work geometry for one (format, H, I).
-template <int FMT, int H, int I>
+// Work geometry for one (routed format, shared format, H, I).
+template <int FMT, int SFMT, int H, int I>
 struct Geo {
   using GU = GateUpGeo<FMT, H>;     // routed gate/up rows per wave item
-  using SGU = GateUpGeo<kBf16, H>;  // shared gate/up
+  using SGU = GateUpGeo<SFMT, H>;   // shared gate/up
   using DN = DownGeo<FMT, I>;       // routed down rows per wave item
-  using SDN = DownGeo<kBf16, I>;    // shared down
+  using SDN = DownGeo<SFMT, I>;     // shared down
   static constexpr int N_GU = I / GU::RP;  // wave items per expert
   static constexpr int N_DN = H / DN::RW;
   static constexpr int CB = DN::RW > 32 ? DN::RW : 32;  // combine rows per item
@@ -743,10 +746,10 @@ __device__ __forceinline__ int owner_block(const Route &R, const int *cum, int s
   return b < nb ? b : nb - 1;
 }
 
-template <int FMT, int H, int I>
+template <int FMT, int SFMT, int H, int I>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
 decode_kernel(Params P) {
-  using Gm = Geo<FMT, H, I>;
+  using Gm = Geo<FMT, SFMT, H, I>;
   using DnMap = RowMap<FMT, I>;
   constexpr int GU_RSZ = FMT == kNvfp4 ? H / 2 : H * 2;  // routed row bytes (w13)
   constexpr int DN_RSZ = FMT == kNvfp4 ? I / 2 : I * 2;  // routed row bytes (w2)
@@ -805,19 +808,28 @@ decode_kernel(Params P) {
 
   // ---- phase A2: shared gate/up, one row-pair item per wave (item j:
   // block sh0 + j % nbs, wave j / nbs), every token.
+  // (an NVFP4 shared expert: E2M1 codes, E4M3 block scales and one global
+  // scale per matrix, the routed experts' rule)
+  constexpr bool kNvShared = SFMT == kNvfp4;
+  constexpr size_t kSguBytes = kNvShared ? (size_t)2 * I * H / 2 : (size_t)2 * I * H * 2;
+  constexpr size_t kSdnBytes = kNvShared ? (size_t)H * I / 2 : (size_t)H * I * 2;
   if (P.sgu) {
-    const __amdgpu_buffer_rsrc_t rs_w = make_rsrc(P.sgu, (size_t)2 * I * H * 2);
+    const __amdgpu_buffer_rsrc_t rs_w = make_rsrc(P.sgu, kSguBytes);
+    const __amdgpu_buffer_rsrc_t rs_s =
+        make_rsrc(kNvShared ? (const void *)P.ssgu : (const void *)P.sgu,
+                  kNvShared ? (size_t)2 * I * (H / 16) : 0);
     const __amdgpu_buffer_rsrc_t rs_o = make_rsrc(P.sact, (size_t)P.M * I * 2);
+    const float alpha = kNvShared ? *P.asgu : 1.0f;
     for (int j = (bs >= 0 && wv < nsg) ? bs + nbs * wv : P.n_sgu; j < P.n_sgu; j += nbs * nsg) {
       const int n_base = j * Gm::SGU::RP;
-      GateUpW<kBf16, H, I> W;
-      gate_up_load(W, rs_w, 0u, rs_w, 0u, n_base);
+      GateUpW<SFMT, H, I> W;
+      gate_up_load(W, rs_w, 0u, rs_s, 0u, n_base);
       wait_x();
       TRACE(P, 9);
       for (int g0 = 0; g0 < P.M; g0 += kWave) {
         const int nt = min(kWave, P.M - g0);
-        gate_up_compute<kBf16, H, I>(P, W, 1.0f, nt, [g0](int i) { return g0 + i; },
-                                     x_all ? xs : nullptr, ob);
+        gate_up_compute<SFMT, H, I>(P, W, alpha, nt, [g0](int i) { return g0 + i; },
+                                    x_all ? xs : nullptr, ob);
         store_results<Gm::SGU::RP>(
             rs_o, lane < nt ? (uint32_t)(((g0 + lane) * I + n_base) * 2) : kOOB, ob);
       }
@@ -830,8 +842,12 @@ decode_kernel(Params P) {
   // sh0 + j % nbs, wave nsg + j / nbs), after every shared gate/up block.
   // sact is staged in a part of the staging area that x does not use.
   if (P.sgu) {
-    const __amdgpu_buffer_rsrc_t rs_w = make_rsrc(P.sdown, (size_t)H * I * 2);
+    const __amdgpu_buffer_rsrc_t rs_w = make_rsrc(P.sdown, kSdnBytes);
+    const __amdgpu_buffer_rsrc_t rs_s =
+        make_rsrc(kNvShared ? (const void *)P.ssdown : (const void *)P.sdown,
+                  kNvShared ? (size_t)H * (I / 16) : 0);
     const __amdgpu_buffer_rsrc_t rs_o = make_rsrc(P.sh, (size_t)P.M * H * 2);
+    const float alpha = kNvShared ? *P.asdown : 1.0f;
     const int free_el = kXLdsBytes / 2 - (x_all ? P.M * H : 0);
     const int per = free_el / max(1, min(nsd, kWaves));  // bf16 per shared-down wave
     // the wave's slice when the free part of the staging area is too small
@@ -844,8 +860,8 @@ decode_kernel(Params P) {
     for (int j = (bs >= 0 && ws >= 0 && ws < nsd) ? bs + nbs * ws : P.n_sdn; j < P.n_sdn;
          j += nbs * nsd) {
       const int h_base = j * Gm::SDN::RW;
-      DownW<kBf16, I> W;
-      down_load(W, rs_w, 0u, rs_w, 0u, h_base);
+      DownW<SFMT, I> W;
+      down_load(W, rs_w, 0u, rs_s, 0u, h_base);
       if (!waited) {
         // the block's first shared down wave polls the flags, the others
         // wait for its word in LDS
@@ -866,7 +882,7 @@ decode_kernel(Params P) {
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         for (int t = 0; t < nt; ++t)
-          down_one<kBf16, H, I, kSrcLds>(W, sl + (size_t)t * I, 1.0f, t, ob);
+          down_one<SFMT, H, I, kSrcLds>(W, sl + (size_t)t * I, alpha, t, ob);
         store_results<Gm::SDN::RW>(
             rs_o, lane < nt ? (uint32_t)(((g0 + lane) * H + h_base) * 2) : kOOB, ob);
       }
@@ -1141,6 +1157,13 @@ decode_kernel(Params P) {
           }
 #pragma unroll
           for (int u = 0; u < 4; ++u) shv[u] = bf16_to_f32(sv[u]);
+        } else if (P.sh_ext) {
+          // a precomputed shared output: an input, complete before the launch
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int o = min(u * kWave + lane, nt * Gm::CB - 1);
+            shv[u] = bf16_to_f32(P.sh_ext[(size_t)(t0 + o / Gm::CB) * H + h0 + o % Gm::CB]);
+          }
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): y is in LDS
         // The lane's four outputs advance together over the pairs, so their
@@ -1176,7 +1199,9 @@ decode_kernel(Params P) {
             if ((unsigned)R.ids[p] < (unsigned)P.E)
               acc += (double)R.tw[p] * (double)bf16_to_f32(ld_dev(&P.y[(size_t)p * H + h0 + hh]));
           }
-          const float sv = P.sgu ? bf16_to_f32(ld_dev(&P.sh[(size_t)t0 * H + h0 + hh])) : 0.0f;
+          const float sv = P.sgu      ? bf16_to_f32(ld_dev(&P.sh[(size_t)t0 * H + h0 + hh]))
+                           : P.sh_ext ? bf16_to_f32(P.sh_ext[(size_t)t0 * H + h0 + hh])
+                                      : 0.0f;
           P.out[(size_t)t0 * H + h0 + hh] = (uint16_t)f32_to_bf16(round_bf16((float)acc) + sv);
         }
       }
@@ -1222,9 +1247,9 @@ hipError_t chained_launch(int dev, hipStream_t st, F &&launch_fn) {
   return hipSuccess;
 }
 
-template <int FMT, int H, int I>
+template <int FMT, int SFMT, int H, int I>
 hipError_t launch(Params P, hipStream_t st) {
-  using Gm = Geo<FMT, H, I>;
+  using Gm = Geo<FMT, SFMT, H, I>;
   static thread_local GridInfo info[64];  // [device]
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -1237,7 +1262,7 @@ hipError_t launch(Params P, hipStream_t st) {
   if (gi.nb == 0) {
     // Blocks resident at once: the grid (one block per compute unit).
     int per_cu = 0, cus = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<FMT, H, I>, kThreads,
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<FMT, SFMT, H, I>, kThreads,
                                                      lds);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -1254,7 +1279,7 @@ hipError_t launch(Params P, hipStream_t st) {
   if (P.nb > kMaxSharedBlocks) return hipErrorInvalidValue;
   return chained_launch(dev, st, [&](hipEvent_t stop) {
     void *args[] = {&P};
-    return hipExtLaunchKernel(reinterpret_cast<const void *>(&decode_kernel<FMT, H, I>), dim3(P.nb),
+    return hipExtLaunchKernel(reinterpret_cast<const void *>(&decode_kernel<FMT, SFMT, H, I>), dim3(P.nb),
                               dim3(kThreads), args, lds, st, nullptr, stop, 0);
   });
 }
@@ -1287,6 +1312,11 @@ hipError_t launch_decode(int fmt, const DecodeArgs &a, hipStream_t st) {
   P.a2 = a.a2;
   P.sgu = a.sgu;
   P.sdown = a.sdown;
+  P.ssgu = a.ssgu;
+  P.ssdown = a.ssdown;
+  P.asgu = a.asgu;
+  P.asdown = a.asdown;
+  P.sh_ext = a.sh_ext;
   P.ids_in = a.ids_in;
   P.tw_in = a.tw_in;
   P.logits = a.logits;
@@ -1310,7 +1340,9 @@ hipError_t launch_decode(int fmt, const DecodeArgs &a, hipStream_t st) {
 #endif
 #define FLINT_DECODE(HH, II)                                                \
   if (a.H == HH && a.I == II)                                               \
-    return fmt == kNvfp4 ? launch<kNvfp4, HH, II>(P, st) : launch<kBf16, HH, II>(P, st);
+    return fmt == kBf16   ? launch<kBf16, kBf16, HH, II>(P, st)                    \
+           : a.ssgu ? launch<kNvfp4, kNvfp4, HH, II>(P, st)                       \
+                    : launch<kNvfp4, kBf16, HH, II>(P, st);
   FLINT_DECODE(2048, 768)
   FLINT_DECODE(256, 128)
   FLINT_DECODE(256, 256)

@@ -46,7 +46,10 @@ struct DecodeArgs {
   const float *a13;
   const uint8_t *w2, *s2;
   const float *a2;
-  const uint8_t *sgu, *sdown;   // shared expert (bf16), NULL = none
+  const uint8_t *sgu, *sdown;   // shared expert (bf16, or E2M1 codes), NULL = none
+  const uint8_t *ssgu, *ssdown; // NVFP4 shared expert: block scales (NULL: bf16 shared)
+  const float *asgu, *asdown;   // NVFP4 shared expert: device global scales
+  const uint16_t *sh_ext;       // precomputed shared output [M, H] (then sgu is NULL)
   const int32_t *ids_in;        // forced routing, NULL = route
   const float *tw_in;
   uint16_t *logits;
@@ -114,7 +117,8 @@ hipError_t launch_plan(const int32_t *ids, int M, int E, int top_k, const Plan &
                        hipStream_t st);
 
 // The whole decode block in one launch (fmt of the routed experts; the
-// shared expert, if any, is bf16 with SI == I).
+// shared expert, if any, has SI == I and is bf16, or NVFP4 when a.ssgu is
+// set and the routed experts are NVFP4).
 hipError_t launch_decode(int fmt, const DecodeArgs &a, hipStream_t st);
 
 // Whether the decode kernel is compiled for this (H, I) (both formats).
@@ -157,8 +161,6 @@ bool grouped_shape_supported(int H, int I, int SI);
 // Residual add + RMS norm rows (norm.hip): res_out = bf16(a + r), xn_out =
 // bf16((s * rsqrt(mean(s^2) + eps)) * w) for M rows of H.
 bool add_rmsnorm_supported(int H);
-// out[i] = bf16(fp32(out[i]) + fp32(sh[i])) for n bf16 values (n % 8 == 0).
-hipError_t launch_add_bf16(uint16_t *out, const uint16_t *sh, size_t n, hipStream_t st);
 hipError_t launch_add_rmsnorm(const uint16_t *a, const uint16_t *r, const uint16_t *w, float eps, int M,
                               int H, uint16_t *res_out, uint16_t *xn_out, hipStream_t st);
 

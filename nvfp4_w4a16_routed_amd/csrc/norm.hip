@@ -72,27 +72,7 @@ __global__ void __launch_bounds__(kNormThreads) add_rmsnorm_kernel(const uint16_
   }
 }
 
-// out = bf16(fp32(out) + fp32(sh)), 8 values per thread: the rule's last
-// step when the shared output comes from the caller.
-__global__ void __launch_bounds__(256) add_bf16_kernel(uint16_t *__restrict__ out,
-                                                       const uint16_t *__restrict__ sh, size_t n8) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const u32x4_t o = load16(out + 8 * i), s = load16(sh + 8 * i);
-  u32x4_t v;
-#pragma unroll
-  for (int d = 0; d < 4; ++d) v[d] = pack_bf16x2(bf16_lo(o[d]) + bf16_lo(s[d]), bf16_hi(o[d]) + bf16_hi(s[d]));
-  *reinterpret_cast<u32x4_t *>(out + 8 * i) = v;
-}
-
 }  // namespace
-
-hipError_t launch_add_bf16(uint16_t *out, const uint16_t *sh, size_t n, hipStream_t st) {
-  const size_t n8 = n / 8;
-  if (n8 == 0) return hipSuccess;
-  hipLaunchKernelGGL(add_bf16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, out, sh, n8);
-  return hipGetLastError();
-}
 
 bool add_rmsnorm_supported(int H) { return H > 0 && H % 8 == 0 && H <= kNormThreads * 8 * kNormChunks; }
 

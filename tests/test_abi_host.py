@@ -85,8 +85,14 @@ def test_decode_rejects_bad_arguments():
     assert _decode(shared=sh) == -2
     sh = fm.SharedExpert(None, None, 0, MIS, None)
     assert _decode(shared=sh) == -3        # precomputed shared output, misaligned
+    sh = fm.SharedExpert(A, A, 768, None, None, A, None, A, A)
+    assert _decode(shared=sh) == -1        # an NVFP4 shared expert without its down scales
+    sh = fm.SharedExpert(A, A, 768, None, None, MIS, A, A, A)
+    assert _decode(shared=sh) == -3
+    sh = fm.SharedExpert(A, A, 512, None, None, A, A, A, A)
+    assert _decode(shared=sh) == -2        # the decode kernel's shared expert is I wide
     sh = fm.SharedExpert(A, A, 768, None, None, A, A, A, A)
-    assert _decode(shared=sh) == -2        # an NVFP4 shared expert: grouped path only
+    assert _decode(shared=sh, ws_bytes=1024) == -4  # accepted up to the workspace check
     dbg = fm.MoeDebug(A, None, None, None, None, None, None, None, None)
     assert _decode(dbg=dbg) == -1          # forced ids without weights
     assert _decode(M=0, x=None) == 0       # empty batch: valid no-op
@@ -119,6 +125,10 @@ def test_bf16_decode_and_grouped_reject_bad_arguments():
     w = fm.Bf16Experts(MIS, A)
     assert L.flint_moe_bf16_decode(A, A, ctypes.byref(w), None, 8, 2048, 128, 768, 8, A, None, A,
                                    1 << 30, None) == -3
+    w = fm.Bf16Experts(A, A)
+    sh = fm.SharedExpert(A, A, 768, None, None, A, A, A, A)  # NVFP4 shared: NVFP4 experts only
+    assert L.flint_moe_bf16_decode(A, A, ctypes.byref(w), ctypes.byref(sh), 8, 2048, 128, 768, 8, A,
+                                   None, A, 1 << 30, None) == -2
 
 
 def _grouped(M=8, H=2048, E=128, I=768, k=8, shared=None, ws_bytes=1 << 62):

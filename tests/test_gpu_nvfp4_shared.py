@@ -70,3 +70,88 @@ def test_grouped_nvfp4_shared_expert(M, H, SI):
     assert ulps.size == 0 or ulps.max() <= 2.0
     print(f"  near-tie flips {int((~same).sum())}, max ulp(m) {ulps.max() if ulps.size else 0:.3f}",
           flush=True)
+
+
+def _oracle_nv_shared(x, shw, H, SI):
+    """The NVFP4 shared expert under the routed rule, one expert that every
+    token selects: (sact, sh) bf16 bits."""
+    one = np.zeros((x.shape[0], 1), dtype=np.int32)
+    sact = oracle.gate_up(x, one, 1, shw, SI)
+    return sact, oracle.down(sact, one, shw, H)
+
+
+def _check_nv_shared_run(inp, shw, r, label):
+    """Stages of a decode run with an NVFP4 shared expert against the oracle."""
+    cfg = inp["cfg"]
+    M, H, SI, k = cfg["M"], cfg["H"], cfg["I"], cfg["top_k"]
+    G.stagewise_routing(inp, r)
+    G.stagewise_routed(inp, r)
+    one = np.zeros((M, 1), dtype=np.int32)
+    ref_sact, det = oracle.gate_up(inp["x"], one, 1, shw, SI, want_detail=True)
+    G.check_act(r["sact"], ref_sact, det, label + " nvfp4 shared gate/up")
+    ref_sh, det2 = oracle.down(r["sact"], one, shw, H, want_detail=True)
+    G.check_y(r["sh"], ref_sh, det2, label + " nvfp4 shared down")
+    out_c, _ = oracle.combine(r["y"], r["tw"], r["sh"], k)
+    assert np.array_equal(r["out"], out_c), "combine differs"
+    _, own_sh = _oracle_nv_shared(inp["x"], shw, H, SI)
+    G.end_to_end(inp, r, lambda *a: print(*a, flush=True), sh_in=own_sh,
+                 extra=dict(path=label + " nvfp4 shared"))
+
+
+@pytest.mark.parametrize("path,M,H,I,E,k", [("decode", 8, 2048, 768, 128, 8),
+                                            ("decode", 5, 256, 128, 16, 4),
+                                            ("noalloc", 3, 512, 256, 32, 8)])
+def test_decode_nvfp4_shared_expert(path, M, H, I, E, k):
+    print(f"decode NVFP4 shared expert path={path} M={M} H={H} I={I} E={E} k={k}", flush=True)
+    inp = synth.make_small(960 + M, M=M, H=H, E=E, I=I, SI=0, top_k=k, router_std=0.3)
+    shw = synth.nvfp4_experts(961 + M, 1, H, I)
+    d = G.device_inputs(inp)
+    shd = {kk: G.dev(v) for kk, v in shw.items()}
+    z = lambda shape, dt: torch.empty(shape, dtype=dt, device="cuda")
+    dbg = dict(logits_out=z((M, E), torch.int16), ids_out=z((M, k), torch.int32),
+               tw_out=z((M, k), torch.float32), act_out=z((M * k, I), torch.int16),
+               y_out=z((M * k, H), torch.int16), sact_out=z((M, I), torch.int16),
+               sh_out=z((M, H), torch.int16))
+    if path == "noalloc":
+        out = fm.flint_moe_decode_noalloc(d["x"], d["router"], G.experts_of(d), shd, k, debug=dbg)
+    else:
+        ws = fm.make_workspace(M, H, E, I, I, k)
+        out = fm.flint_moe_decode(d["x"], d["router"], G.experts_of(d), shd, k, ws, debug=dbg)
+    torch.cuda.synchronize()
+    r = {kk[:-4]: G.host(v) for kk, v in dbg.items()}
+    r["out"] = G.host(out)
+    _check_nv_shared_run(inp, shw, r, path)
+
+
+def test_ll_nvfp4_shared_expert():
+    """flint_moe_ll (residual add + RMS norm, then the decode block) with an
+    NVFP4 shared expert, as the pages' fused decode block holds it."""
+    print("flint_moe_ll with an NVFP4 shared expert, M=8 E=128", flush=True)
+    M, E, k = 8, 128, 8
+    inp = synth.make_inputs(1, M=M)
+    cfg = inp["cfg"]
+    H, I = cfg["H"], cfg["I"]
+    shw = synth.nvfp4_experts(977, 1, H, I)
+    ll = synth.make_ll_inputs(978, M, H)
+    d = G.device_inputs(inp)
+    shd = {kk: G.dev(v) for kk, v in shw.items()}
+    ws = fm.make_workspace(M, H, E, I, I, k)
+    z = lambda shape, dt: torch.empty(shape, dtype=dt, device="cuda")
+    dbg = dict(logits_out=z((M, E), torch.int16), ids_out=z((M, k), torch.int32),
+               tw_out=z((M, k), torch.float32), act_out=z((M * k, I), torch.int16),
+               y_out=z((M * k, H), torch.int16), sact_out=z((M, I), torch.int16),
+               sh_out=z((M, H), torch.int16))
+    out, res, xn = fm.flint_moe_ll(G.dev(ll["attn_out"]), G.dev(ll["residual"]), G.dev(ll["ln_weight"]),
+                                   ll["eps"], d["router"], G.experts_of(d), shd, k, ws, debug=dbg)
+    torch.cuda.synchronize()
+    res_ref, xn_ref = oracle.add_rms_norm(ll["attn_out"], ll["residual"], ll["ln_weight"], ll["eps"])
+    assert np.array_equal(G.host(res), res_ref)
+    xg = G.host(xn)
+    assert np.all(np.abs(G.bf(xg) - G.bf(xn_ref)) <= G.ulp_bf16(G.bf(xn_ref))), "xn beyond one bf16 ulp"
+    inp2 = dict(inp)
+    inp2["x"] = xg
+    inp2.pop("sgu", None)
+    inp2.pop("sdown", None)
+    r = {kk[:-4]: G.host(v) for kk, v in dbg.items()}
+    r["out"] = G.host(out)
+    _check_nv_shared_run(inp2, shw, r, "ll")
