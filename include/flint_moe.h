@@ -33,7 +33,8 @@
  *      decode entry points: M <= 64, M * top_k <= 512, (H, I) one of
  *        (2048, 768), (256, 128), (256, 256), (512, 128), (512, 256),
  *        shared width SI == I (or no shared expert);
- *      flint_moe_grouped: H % 128 == 0, 128 <= H <= 8192; I % 64 == 0,
+ *      flint_moe_grouped, flint_moe_bf16_grouped: H % 128 == 0,
+ *        128 <= H <= 8192; I % 64 == 0,
  *        64 <= I <= 8192; a shared expert has SI % 64 == 0, 64 <= SI <=
  *        8192; M * H * 2, M * top_k * I * 2 and M * SI * 2 bytes each
  *        below 2^31 (the GEMMs address x, act and sact through 32-bit
@@ -272,6 +273,17 @@ int flint_moe_bf16_decode(const uint16_t *x, const uint16_t *router,
                           int M, int H, int E, int I, int top_k, uint16_t *out,
                           const flint_moe_debug *dbg, void *ws, size_t ws_bytes,
                           void *stream);
+
+/* The MoE block on BF16 experts for any M >= 1 with grouped MFMA GEMMs (page
+ * "vllm.models.flint.model", FlintSparseMoeBlock: BF16 experts use the decode
+ * kernels for small batches and a grouped MoE GEMM otherwise; the rule is
+ * flint_moe_bf16_decode's).  Shapes, limits, shared expert and errors as
+ * flint_moe_grouped. */
+int flint_moe_bf16_grouped(const uint16_t *x, const uint16_t *router,
+                           const flint_bf16_experts *w, const flint_shared_expert *shared,
+                           int M, int H, int E, int I, int top_k, uint16_t *out,
+                           const flint_moe_debug *dbg, void *ws, size_t ws_bytes,
+                           void *stream);
 
 #ifdef __cplusplus
 }

@@ -30,7 +30,7 @@ EXPORTS = ("flint_status_str", "flint_last_hip_error", "flint_moe_workspace_byte
            "flint_moe_workspace_init", "flint_nvfp4_dequant", "flint_moe_topk",
            "flint_moe_route", "flint_moe_decode", "flint_moe_grouped",
            "flint_moe_bf16_decode", "flint_moe_ll", "flint_moe_wait_errors",
-           "flint_moe_decode_noalloc")
+           "flint_moe_decode_noalloc", "flint_moe_bf16_grouped")
 
 
 class FlintError(RuntimeError):
@@ -103,7 +103,8 @@ def lib() -> ctypes.CDLL:
         L.flint_moe_route.restype = I32
         L.flint_moe_route.argtypes = [P, P, I32, I32, I32, I32, P, P, P, P, ctypes.c_size_t, P]
         moe_args = [P, P, P, P, I32, I32, I32, I32, I32, P, P, P, ctypes.c_size_t, P]
-        for name in ("flint_moe_decode", "flint_moe_grouped", "flint_moe_bf16_decode"):
+        for name in ("flint_moe_decode", "flint_moe_grouped", "flint_moe_bf16_decode",
+                     "flint_moe_bf16_grouped"):
             fn = getattr(L, name)
             fn.restype = I32
             fn.argtypes = moe_args
@@ -308,6 +309,15 @@ def flint_moe_grouped(x, router, experts: dict, shared, top_k: int, ws, out=None
     E, I = experts["w13"].shape[0], experts["w2"].shape[2] * 2
     st = nvfp4_experts_struct(*(experts[k] for k in ("w13", "s13", "a13", "w2", "s2", "a2")))
     return _moe_call("flint_moe_grouped", st, x, router, shared, I, E, top_k, ws, out, debug, stream)
+
+
+def flint_moe_bf16_grouped(x, router, experts: dict, shared, top_k: int, ws, out=None, debug=None,
+                           stream=None):
+    """experts: dict w13 [E,2I,H] bf16, w2 [E,H,I] bf16; any M."""
+    E, I = experts["w13"].shape[0], experts["w2"].shape[2]
+    st = Bf16Experts(_ptr(experts["w13"]), _ptr(experts["w2"]))
+    return _moe_call("flint_moe_bf16_grouped", st, x, router, shared, I, E, top_k, ws, out, debug,
+                     stream)
 
 
 def flint_moe_bf16_decode(x, router, experts: dict, shared, top_k: int, ws, out=None, debug=None,

@@ -132,12 +132,22 @@ int check_shared(const flint_shared_expert *sh, int H, int I, bool allow_nvfp4) 
   return FLINT_OK;
 }
 
-// The decode pipeline shared by the NVFP4 and BF16 experts.
+// Inputs and outputs of the residual add + RMS norm formed inside the
+// decode kernel (flint_moe_ll).
+struct NormIn {
+  const uint16_t *a, *r, *w;
+  float eps;
+  uint16_t *res, *xn;
+};
+
+// The decode pipeline shared by the NVFP4 and BF16 experts (norm: the
+// residual add + RMS norm in front, formed inside the kernel; x is then
+// norm->xn, written by the kernel).
 int run_decode(int fmt, const uint16_t *x, const uint16_t *router, const void *w13,
                const uint8_t *s13, const float *a13, const void *w2, const uint8_t *s2,
                const float *a2, const flint_shared_expert *shared, int M, int H, int E, int I,
                int top_k, uint16_t *out, const flint_moe_debug *dbg, void *ws,
-               size_t ws_bytes, hipStream_t st) {
+               size_t ws_bytes, hipStream_t st, const NormIn *norm = nullptr) {
   const bool ext_sh = shared && shared->sh_in;  // precomputed shared output
   const bool has_shared = !ext_sh && shared && shared->w_gu;
   const int SI = has_shared ? shared->SI : 0;
@@ -174,6 +184,14 @@ int run_decode(int fmt, const uint16_t *x, const uint16_t *router, const void *w
   a.asgu = nv_sh ? shared->a_gu : nullptr;
   a.asdown = nv_sh ? shared->a_down : nullptr;
   a.sh_ext = ext_sh ? shared->sh_in : nullptr;
+  if (norm) {
+    a.ln_a = norm->a;
+    a.ln_r = norm->r;
+    a.ln_w = norm->w;
+    a.eps = norm->eps;
+    a.res_out = norm->res;
+    a.xn_out = norm->xn;
+  }
   a.ids_in = forced ? dbg->ids_in : nullptr;
   a.tw_in = forced ? dbg->tw_in : nullptr;
   a.logits = logits;
@@ -204,6 +222,93 @@ int run_decode(int fmt, const uint16_t *x, const uint16_t *router, const void *w
   if (e == hipSuccess) e = launch_decode(fmt, a, st);
   for (int i = 1; i < FLINT_STAGE_EVENTS && e == hipSuccess; ++i) e = mark(i);
   return hip_status(e);
+}
+
+// The grouped pipeline shared by the NVFP4 and BF16 experts: a holds the
+// expert weights (checked by the caller); everything else is checked here.
+int run_grouped(GroupedArgs a, bool have_w, const uint16_t *x, const uint16_t *router,
+                const flint_shared_expert *shared, int M, int H, int E, int I, int top_k,
+                uint16_t *out, const flint_moe_debug *dbg, void *ws, size_t ws_bytes,
+                void *stream) {
+  const bool forced = dbg && dbg->ids_in;
+  const bool ext_sh = shared && shared->sh_in;  // precomputed shared output
+  const bool has_shared = !ext_sh && shared && shared->w_gu;
+  const int SI = has_shared ? shared->SI : 0;
+  if (M < 0 || top_k < 1 || E < 1 || top_k > E || E > kMaxExperts) return FLINT_ERR_SHAPE;
+  if (!grouped_shape_supported(H, I, SI)) return FLINT_ERR_SHAPE;
+  if (has_shared && SI < 64) return FLINT_ERR_SHAPE;  // a shared expert has a width
+  // x, act and sact are read through buffer descriptors (byte offsets below
+  // 2^31)
+  const long long kDesc = 1ll << 31;
+  if ((long long)M * H * 2 >= kDesc || (long long)M * top_k * I * 2 >= kDesc ||
+      (long long)M * SI * 2 >= kDesc)
+    return FLINT_ERR_SHAPE;
+  if (M == 0) return FLINT_OK;  // nothing to compute; no pointer is used
+  if (!x || !have_w || !out || (!forced && !router)) return FLINT_ERR_NULL;
+  if (forced && !dbg->tw_in) return FLINT_ERR_NULL;
+  if (has_shared && !shared->w_down) return FLINT_ERR_NULL;
+  const bool nv_sh = has_shared && shared->s_gu;
+  if (nv_sh && (!shared->s_down || !shared->a_gu || !shared->a_down)) return FLINT_ERR_NULL;
+  if (nv_sh && (!aligned16(shared->s_gu) || !aligned16(shared->s_down) || !aligned16(shared->a_gu) ||
+                !aligned16(shared->a_down)))
+    return FLINT_ERR_ALIGN;
+  if (!ws) return FLINT_ERR_WORKSPACE;
+  if (!aligned16(x) || (router && !aligned16(router)) || !aligned16(out) || !aligned16(ws) ||
+      (has_shared && (!aligned16(shared->w_gu) || !aligned16(shared->w_down))) ||
+      (ext_sh && !aligned16(shared->sh_in)))
+    return FLINT_ERR_ALIGN;
+  Workspace W = carve_workspace(ws, M, H, E, I, SI, top_k);
+  if (W.bytes > ws_bytes) return FLINT_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  a.x = x;
+  a.router = router;
+  a.sgu = has_shared ? shared->w_gu : nullptr;
+  a.sdown = has_shared ? shared->w_down : nullptr;
+  a.sh_ext = ext_sh ? shared->sh_in : nullptr;
+  a.sh_ready = ext_sh ? shared->sh_ready : nullptr;
+  a.s_gu = nv_sh ? shared->s_gu : nullptr;
+  a.s_down = nv_sh ? shared->s_down : nullptr;
+  a.a_gu = nv_sh ? shared->a_gu : nullptr;
+  a.a_down = nv_sh ? shared->a_down : nullptr;
+  a.sh_lists = W.sh_lists;
+  a.sh_counts = W.sh_counts;
+  a.ids_in = forced ? dbg->ids_in : nullptr;
+  a.logits = (dbg && dbg->logits_out) ? dbg->logits_out : W.logits;
+  int32_t *ids = (dbg && dbg->ids_out) ? dbg->ids_out : W.ids;
+  float *tw = (dbg && dbg->tw_out) ? dbg->tw_out : W.tw;
+  if (forced) {
+    // the given routing, copied where the outputs were asked for
+    const size_t P = (size_t)M * top_k;
+    if (dbg->ids_out) {
+      hipError_t e = hipMemcpyAsync(ids, dbg->ids_in, 4 * P, hipMemcpyDeviceToDevice, st);
+      if (e != hipSuccess) return hip_status(e);
+    } else {
+      ids = const_cast<int32_t *>(dbg->ids_in);
+    }
+    if (dbg->tw_out) {
+      hipError_t e = hipMemcpyAsync(tw, dbg->tw_in, 4 * P, hipMemcpyDeviceToDevice, st);
+      if (e != hipSuccess) return hip_status(e);
+    } else {
+      tw = const_cast<float *>(dbg->tw_in);
+    }
+  }
+  a.ids = ids;
+  a.tw = tw;
+  a.lists = W.lists;
+  a.counts = W.counts;
+  a.act = (dbg && dbg->act_out) ? dbg->act_out : W.act;
+  a.y = (dbg && dbg->y_out) ? dbg->y_out : W.y;
+  a.sact = (dbg && dbg->sact_out) ? dbg->sact_out : W.sact;
+  a.sh = (dbg && dbg->sh_out) ? dbg->sh_out : W.sh;
+  a.out = out;
+  a.events = dbg ? dbg->stage_events : nullptr;
+  a.M = M;
+  a.H = H;
+  a.E = E;
+  a.I = I;
+  a.SI = SI;
+  a.top_k = top_k;
+  return hip_status(launch_grouped(a, st));
 }
 
 }  // namespace
@@ -368,6 +473,13 @@ int flint_moe_ll(const uint16_t *attn_out, const uint16_t *residual, const uint1
       !aligned16(w->a2))
     return FLINT_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
+  if ((long)M * H * 2 <= kDecodeXStage) {
+    // every block of the decode kernel forms the normed rows itself (they
+    // fit its LDS): one launch
+    const NormIn norm{attn_out, residual, ln_weight, eps, residual_out, xn_out};
+    return run_decode(kNvfp4, xn_out, router, w->w13, w->s13, w->a13, w->w2, w->s2, w->a2, shared,
+                      M, H, E, I, top_k, out, dbg, ws, ws_bytes, s, &norm);
+  }
   if (hipError_t e = launch_add_rmsnorm(attn_out, residual, ln_weight, eps, M, H, residual_out, xn_out, s);
       e != hipSuccess)
     return hip_status(e);
@@ -398,95 +510,37 @@ int flint_moe_grouped(const uint16_t *x, const uint16_t *router, const flint_nvf
                       const flint_shared_expert *shared, int M, int H, int E, int I, int top_k,
                       uint16_t *out, const flint_moe_debug *dbg, void *ws, size_t ws_bytes,
                       void *stream) {
-  const bool forced = dbg && dbg->ids_in;
-  const bool ext_sh = shared && shared->sh_in;  // precomputed shared output
-  const bool has_shared = !ext_sh && shared && shared->w_gu;
-  const int SI = has_shared ? shared->SI : 0;
-  if (M < 0 || top_k < 1 || E < 1 || top_k > E || E > kMaxExperts) return FLINT_ERR_SHAPE;
-  if (!grouped_shape_supported(H, I, SI)) return FLINT_ERR_SHAPE;
-  if (has_shared && SI < 64) return FLINT_ERR_SHAPE;  // a shared expert has a width
-  // x, act and sact are read through buffer descriptors (byte offsets below
-  // 2^31)
-  const long long kDesc = 1ll << 31;
-  if ((long long)M * H * 2 >= kDesc || (long long)M * top_k * I * 2 >= kDesc ||
-      (long long)M * SI * 2 >= kDesc)
-    return FLINT_ERR_SHAPE;
-  if (M == 0) return FLINT_OK;  // nothing to compute; no pointer is used
-  if (!x || !w || !out || (!forced && !router)) return FLINT_ERR_NULL;
-  if (!w->w13 || !w->s13 || !w->a13 || !w->w2 || !w->s2 || !w->a2) return FLINT_ERR_NULL;
-  if (forced && !dbg->tw_in) return FLINT_ERR_NULL;
-  if (has_shared && !shared->w_down) return FLINT_ERR_NULL;
-  const bool nv_sh = has_shared && shared->s_gu;
-  if (nv_sh && (!shared->s_down || !shared->a_gu || !shared->a_down)) return FLINT_ERR_NULL;
-  if (nv_sh && (!aligned16(shared->s_gu) || !aligned16(shared->s_down) || !aligned16(shared->a_gu) ||
-                !aligned16(shared->a_down)))
+  if (M > 0 && w && (!w->w13 || !w->s13 || !w->a13 || !w->w2 || !w->s2 || !w->a2))
+    return FLINT_ERR_NULL;
+  if (M > 0 && w && (!aligned16(w->w13) || !aligned16(w->s13) || !aligned16(w->a13) ||
+                     !aligned16(w->w2) || !aligned16(w->s2) || !aligned16(w->a2)))
     return FLINT_ERR_ALIGN;
-  if (!ws) return FLINT_ERR_WORKSPACE;
-  if (!aligned16(x) || (router && !aligned16(router)) || !aligned16(out) || !aligned16(ws) ||
-      !aligned16(w->w13) || !aligned16(w->s13) || !aligned16(w->a13) || !aligned16(w->w2) ||
-      !aligned16(w->s2) || !aligned16(w->a2) ||
-      (has_shared && (!aligned16(shared->w_gu) || !aligned16(shared->w_down))) ||
-      (ext_sh && !aligned16(shared->sh_in)))
-    return FLINT_ERR_ALIGN;
-  Workspace W = carve_workspace(ws, M, H, E, I, SI, top_k);
-  if (W.bytes > ws_bytes) return FLINT_ERR_WORKSPACE;
-  hipStream_t st = (hipStream_t)stream;
   GroupedArgs a{};
-  a.x = x;
-  a.router = router;
-  a.w13 = w->w13;
-  a.s13 = w->s13;
-  a.a13 = w->a13;
-  a.w2 = w->w2;
-  a.s2 = w->s2;
-  a.a2 = w->a2;
-  a.sgu = has_shared ? shared->w_gu : nullptr;
-  a.sdown = has_shared ? shared->w_down : nullptr;
-  a.sh_ext = ext_sh ? shared->sh_in : nullptr;
-  a.sh_ready = ext_sh ? shared->sh_ready : nullptr;
-  a.s_gu = nv_sh ? shared->s_gu : nullptr;
-  a.s_down = nv_sh ? shared->s_down : nullptr;
-  a.a_gu = nv_sh ? shared->a_gu : nullptr;
-  a.a_down = nv_sh ? shared->a_down : nullptr;
-  a.sh_lists = W.sh_lists;
-  a.sh_counts = W.sh_counts;
-  a.ids_in = forced ? dbg->ids_in : nullptr;
-  a.logits = (dbg && dbg->logits_out) ? dbg->logits_out : W.logits;
-  int32_t *ids = (dbg && dbg->ids_out) ? dbg->ids_out : W.ids;
-  float *tw = (dbg && dbg->tw_out) ? dbg->tw_out : W.tw;
-  if (forced) {
-    // the given routing, copied where the outputs were asked for
-    const size_t P = (size_t)M * top_k;
-    if (dbg->ids_out) {
-      hipError_t e = hipMemcpyAsync(ids, dbg->ids_in, 4 * P, hipMemcpyDeviceToDevice, st);
-      if (e != hipSuccess) return hip_status(e);
-    } else {
-      ids = const_cast<int32_t *>(dbg->ids_in);
-    }
-    if (dbg->tw_out) {
-      hipError_t e = hipMemcpyAsync(tw, dbg->tw_in, 4 * P, hipMemcpyDeviceToDevice, st);
-      if (e != hipSuccess) return hip_status(e);
-    } else {
-      tw = const_cast<float *>(dbg->tw_in);
-    }
+  if (w) {
+    a.w13 = w->w13;
+    a.s13 = w->s13;
+    a.a13 = w->a13;
+    a.w2 = w->w2;
+    a.s2 = w->s2;
+    a.a2 = w->a2;
   }
-  a.ids = ids;
-  a.tw = tw;
-  a.lists = W.lists;
-  a.counts = W.counts;
-  a.act = (dbg && dbg->act_out) ? dbg->act_out : W.act;
-  a.y = (dbg && dbg->y_out) ? dbg->y_out : W.y;
-  a.sact = (dbg && dbg->sact_out) ? dbg->sact_out : W.sact;
-  a.sh = (dbg && dbg->sh_out) ? dbg->sh_out : W.sh;
-  a.out = out;
-  a.events = dbg ? dbg->stage_events : nullptr;
-  a.M = M;
-  a.H = H;
-  a.E = E;
-  a.I = I;
-  a.SI = SI;
-  a.top_k = top_k;
-  return hip_status(launch_grouped(a, st));
+  return run_grouped(a, w != nullptr, x, router, shared, M, H, E, I, top_k, out, dbg, ws, ws_bytes,
+                     stream);
+}
+
+int flint_moe_bf16_grouped(const uint16_t *x, const uint16_t *router, const flint_bf16_experts *w,
+                           const flint_shared_expert *shared, int M, int H, int E, int I, int top_k,
+                           uint16_t *out, const flint_moe_debug *dbg, void *ws, size_t ws_bytes,
+                           void *stream) {
+  if (M > 0 && w && (!w->w13 || !w->w2)) return FLINT_ERR_NULL;
+  if (M > 0 && w && (!aligned16(w->w13) || !aligned16(w->w2))) return FLINT_ERR_ALIGN;
+  GroupedArgs a{};
+  if (w) {
+    a.bw13 = w->w13;
+    a.bw2 = w->w2;
+  }
+  return run_grouped(a, w != nullptr, x, router, shared, M, H, E, I, top_k, out, dbg, ws, ws_bytes,
+                     stream);
 }
 
 }  // extern "C"

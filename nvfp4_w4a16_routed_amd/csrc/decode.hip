@@ -59,7 +59,7 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;  // 16
 constexpr int kRouteTokens = 4;           // tokens per routing item (one load round trip)
-constexpr int kXLdsBytes = 65536;         // x staged in LDS when M * H * 2 fits
+constexpr int kXLdsBytes = kDecodeXStage;  // x staged in LDS when M * H * 2 fits
 constexpr int kSliceBytes = 4096;         // per-wave LDS slice (act cache, combine)
 constexpr int kCacheLdsBytes = kWaves * kSliceBytes;
 // Cache-policy operand of a direct global->LDS load that reads at device
@@ -94,6 +94,12 @@ struct Params {
   const uint8_t *ssgu, *ssdown;  // NVFP4 shared expert: E4M3 block scales
   const float *asgu, *asdown;    // NVFP4 shared expert: global scales (device)
   const uint16_t *sh_ext;        // precomputed shared output [M, H], NULL = none
+  // Residual add + RMS norm in front of the block (NULL ln_a: x is given):
+  // every block forms xn = bf16((s * rsqrt(mean s^2 + eps)) * ln_w) with
+  // s = ln_a + ln_r itself; block 0 writes res_out = bf16(s) and xn_out.
+  const uint16_t *ln_a, *ln_r, *ln_w;
+  float eps;
+  uint16_t *res_out, *xn_out;
   const int32_t *ids_in; // forced routing (NULL = route)
   const float *tw_in;
   uint16_t *logits;
@@ -575,8 +581,61 @@ __device__ __forceinline__ void stage_rows(uint16_t *dst, const uint16_t *src, i
 // word (the value and its "written" mark arrive together).  x is read from
 // global memory (it is an input), so the item needs no LDS and can start at
 // once.
+// The residual add and RMS norm of row t (page "vllm.models.flint.ops.moe",
+// _add_rms_norm), by one wave: s = fp32(a + r) (one rounding), the fp32 sum
+// of s^2 (each lane sums its chunks in order with fused multiply-adds, then
+// the fixed DPP tree), inv = 1 / sqrt(sum / H + eps) (correctly rounded),
+// xn = bf16((s * inv) * w).  Lane l holds 16-byte chunks l + 64 i of the
+// row, as route_item reads x.  Every wave that forms a row's xn gets the
+// same bits, so routing and the staged copy agree.
 template <int H>
-__device__ void route_item(const Params &P, int r) {
+__device__ __forceinline__ void norm_row(const Params &P, int t,
+                                         u32x4_t (&xn)[(H / 8 + kWave - 1) / kWave],
+                                         u32x4_t (&res)[(H / 8 + kWave - 1) / kWave]) {
+  constexpr int NC = H / 8, CPL = (NC + kWave - 1) / kWave;
+  const int lane = lane_id();
+  float sv[CPL][8];
+  u32x4_t w[CPL];
+  float ss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane + kWave * i;
+    u32x4_t a{0, 0, 0, 0}, r{0, 0, 0, 0};
+    w[i] = u32x4_t{0, 0, 0, 0};
+    if (c < NC) {  // every load of the row in flight at once
+      a = load16(P.ln_a + (size_t)t * H + c * 8);
+      r = load16(P.ln_r + (size_t)t * H + c * 8);
+      w[i] = load16(P.ln_w + c * 8);
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      sv[i][2 * d] = bf16_lo(a[d]) + bf16_lo(r[d]);
+      sv[i][2 * d + 1] = bf16_hi(a[d]) + bf16_hi(r[d]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < CPL; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(sv[i][e], sv[i][e], ss);
+  ss = group_sum<kWave>(ss);
+  ss = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ss), kWave - 1));
+  const float inv = 1.0f / sqrtf(ss / (float)H + P.eps);
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      xn[i][d] = pack_bf16x2((sv[i][2 * d] * inv) * bf16_lo(w[i][d]),
+                             (sv[i][2 * d + 1] * inv) * bf16_hi(w[i][d]));
+      res[i][d] = pack_bf16x2(sv[i][2 * d], sv[i][2 * d + 1]);
+    }
+  }
+}
+
+// NORM: x is the block's staged normed rows in LDS (xl), formed in front of
+// the routing; wait_x() waits for them (after the router row's loads are
+// issued, so their round trip overlaps the staging).
+template <int H, bool NORM, typename WaitX>
+__device__ void route_item(const Params &P, int r, const uint16_t *xl, WaitX &&wait_x) {
   constexpr int NC = H / 8;
   constexpr int CPL = (NC + kWave - 1) / kWave;
   const int lane = lane_id();
@@ -590,16 +649,28 @@ __device__ void route_item(const Params &P, int r) {
     w[i] = c < NC ? load16(P.router + (size_t)e * H + c * 8) : u32x4_t{0, 0, 0, 0};
   }
   const unsigned long long tag = (unsigned long long)(uint32_t)P.seq << 32;
+  if constexpr (NORM) wait_x();
   for (int g = 0; g < nt; g += 4) {
     u32x4_t xv[4][CPL];
+    if constexpr (NORM) {
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti)
+      for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const int c = lane + kWave * i;
-        xv[ti][i] = (g + ti < nt && c < NC) ? load16(P.x + (size_t)(t0 + g + ti) * H + c * 8)
-                                            : u32x4_t{0, 0, 0, 0};
-      }
+        for (int i = 0; i < CPL; ++i) {
+          const int c = lane + kWave * i;
+          xv[ti][i] = (g + ti < nt && c < NC) ? load16(xl + (size_t)(t0 + g + ti) * H + c * 8)
+                                              : u32x4_t{0, 0, 0, 0};
+        }
+    } else {
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          const int c = lane + kWave * i;
+          xv[ti][i] = (g + ti < nt && c < NC) ? load16(P.x + (size_t)(t0 + g + ti) * H + c * 8)
+                                              : u32x4_t{0, 0, 0, 0};
+        }
+    }
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
       float acc = 0.0f;
@@ -746,7 +817,9 @@ __device__ __forceinline__ int owner_block(const Route &R, const int *cum, int s
   return b < nb ? b : nb - 1;
 }
 
-template <int FMT, int SFMT, int H, int I>
+// NORM: the residual add + RMS norm in front of the block is formed by every
+// block into its x staging area (all of x fits), before the routing items.
+template <int FMT, int SFMT, bool NORM, int H, int I>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
 decode_kernel(Params P) {
   using Gm = Geo<FMT, SFMT, H, I>;
@@ -779,23 +852,50 @@ decode_kernel(Params P) {
   if (P.probe && blockIdx.x == 0 && wv == 0)
     wave_wait_flags(&S->probe, 0, 1, ~P.seq, P.polls, S, kWaitProbe);
 
+  auto wait_x = [&]() {
+    if (x_all) wait_lds_at_least(&R.x_staged, kWaves - 1, S);
+  };
+  if constexpr (NORM) {
+    // The normed rows, formed by every wave but the last of this block
+    // (block 0 also writes them and the residual sum out), before the
+    // routing items that read them here.
+    constexpr int NC = H / 8, CPL = (NC + kWave - 1) / kWave;
+    if (wv < kWaves - 1) {
+      for (int t = wv; t < P.M; t += kWaves - 1) {
+        u32x4_t xn[CPL], rs[CPL];
+        norm_row<H>(P, t, xn, rs);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          const int c = lane + kWave * i;
+          if (c < NC) {
+            *reinterpret_cast<u32x4_t *>(xs + (size_t)t * H + c * 8) = xn[i];
+            if (blockIdx.x == 0) {
+              *reinterpret_cast<u32x4_t *>(P.xn_out + (size_t)t * H + c * 8) = xn[i];
+              *reinterpret_cast<u32x4_t *>(P.res_out + (size_t)t * H + c * 8) = rs[i];
+            }
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      if (lane == 0) atomicAdd(&R.x_staged, 1);
+    }
+  }
+
   // ---- phase A1: routing items, one per wave from the last wave of each
-  // block down (item r: block r % nb); they read x from global memory.
+  // block down (item r: block r % nb); they read x from global memory (the
+  // staged normed rows with NORM).
   for (int r = blockIdx.x + P.nb * (kWaves - 1 - wv); r < P.n_route; r += P.nb * kWaves) {
     __builtin_amdgcn_s_setprio(3);  // on the critical path
-    route_item<H>(P, r);
+    route_item<H, NORM>(P, r, xs, wait_x);
     __builtin_amdgcn_s_setprio(0);
   }
   TRACE(P, 1);
   // All of x in LDS when it fits (shared gate/up and phase B read it
   // there), staged by every wave but the last; R.x_staged counts them.
-  if (x_all && wv < kWaves - 1) {
+  if (!NORM && x_all && wv < kWaves - 1) {
     copy_to_lds<false>(xs, P.x, P.M * H / 8, wv, kWaves - 1);
     if (lane == 0) atomicAdd(&R.x_staged, 1);
   }
-  auto wait_x = [&]() {
-    if (x_all) wait_lds_at_least(&R.x_staged, kWaves - 1, S);
-  };
 
   // Shared-expert items go to every block: shared gate/up items to its
   // first nsg waves, shared down items to the next nsd waves; the remaining
@@ -1247,7 +1347,7 @@ hipError_t chained_launch(int dev, hipStream_t st, F &&launch_fn) {
   return hipSuccess;
 }
 
-template <int FMT, int SFMT, int H, int I>
+template <int FMT, int SFMT, bool NORM, int H, int I>
 hipError_t launch(Params P, hipStream_t st) {
   using Gm = Geo<FMT, SFMT, H, I>;
   static thread_local GridInfo info[64];  // [device]
@@ -1262,7 +1362,7 @@ hipError_t launch(Params P, hipStream_t st) {
   if (gi.nb == 0) {
     // Blocks resident at once: the grid (one block per compute unit).
     int per_cu = 0, cus = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<FMT, SFMT, H, I>, kThreads,
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<FMT, SFMT, NORM, H, I>, kThreads,
                                                      lds);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -1279,7 +1379,7 @@ hipError_t launch(Params P, hipStream_t st) {
   if (P.nb > kMaxSharedBlocks) return hipErrorInvalidValue;
   return chained_launch(dev, st, [&](hipEvent_t stop) {
     void *args[] = {&P};
-    return hipExtLaunchKernel(reinterpret_cast<const void *>(&decode_kernel<FMT, SFMT, H, I>), dim3(P.nb),
+    return hipExtLaunchKernel(reinterpret_cast<const void *>(&decode_kernel<FMT, SFMT, NORM, H, I>), dim3(P.nb),
                               dim3(kThreads), args, lds, st, nullptr, stop, 0);
   });
 }
@@ -1317,6 +1417,12 @@ hipError_t launch_decode(int fmt, const DecodeArgs &a, hipStream_t st) {
   P.asgu = a.asgu;
   P.asdown = a.asdown;
   P.sh_ext = a.sh_ext;
+  P.ln_a = a.ln_a;
+  P.ln_r = a.ln_r;
+  P.ln_w = a.ln_w;
+  P.eps = a.eps;
+  P.res_out = a.res_out;
+  P.xn_out = a.xn_out;
   P.ids_in = a.ids_in;
   P.tw_in = a.tw_in;
   P.logits = a.logits;
@@ -1340,9 +1446,11 @@ hipError_t launch_decode(int fmt, const DecodeArgs &a, hipStream_t st) {
 #endif
 #define FLINT_DECODE(HH, II)                                                \
   if (a.H == HH && a.I == II)                                               \
-    return fmt == kBf16   ? launch<kBf16, kBf16, HH, II>(P, st)                    \
-           : a.ssgu ? launch<kNvfp4, kNvfp4, HH, II>(P, st)                       \
-                    : launch<kNvfp4, kBf16, HH, II>(P, st);
+    return fmt == kBf16 ? launch<kBf16, kBf16, false, HH, II>(P, st)                       \
+           : a.ln_a    ? (a.ssgu ? launch<kNvfp4, kNvfp4, true, HH, II>(P, st)                \
+                                 : launch<kNvfp4, kBf16, true, HH, II>(P, st))                \
+           : a.ssgu    ? launch<kNvfp4, kNvfp4, false, HH, II>(P, st)                         \
+                       : launch<kNvfp4, kBf16, false, HH, II>(P, st);
   FLINT_DECODE(2048, 768)
   FLINT_DECODE(256, 128)
   FLINT_DECODE(256, 256)

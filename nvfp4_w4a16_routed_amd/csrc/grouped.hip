@@ -50,7 +50,10 @@ enum GemmMode {
   kSharedGateUp = 1, // sact[t, n] = bf16(swiglu(x[t] . Wg[n], x[t] . Wu[n]))
   kSharedDown = 2,   // sh[t, h] = bf16(sact[t] . Wd[h])
   kRoutedGateUp = 3, // act[p, n] = bf16(swiglu(a13 x[t(p)] . W13[n], a13 x[t(p)] . W13[I+n]))
-  kRoutedDown = 4    // y[p, h] = bf16(a2 * act[p] . W2[h])
+  kRoutedDown = 4,   // y[p, h] = bf16(a2 * act[p] . W2[h])
+  // BF16 routed experts (no global scale), on gemm_kernel with gathered rows
+  kBf16GateUp = 5,   // act[p, n] = bf16(swiglu(x[t(p)] . W13[e, n], x[t(p)] . W13[e, I+n]))
+  kBf16Down = 6      // y[p, h] = bf16(act[p] . W2[e, h])
 };
 
 struct GemmArgs {
@@ -101,10 +104,14 @@ __device__ __forceinline__ u32x4_t dequant8(uint32_t codes, float scale) {
                  dequant2<3>(codes, scale)};
 }
 
-// The shared expert's products (MODE kSharedGateUp or kSharedDown).
+// Products with bf16 B rows: the shared expert's (MODE kSharedGateUp,
+// kSharedDown: every token, one B matrix) and the BF16 routed experts'
+// (kBf16GateUp, kBf16Down: the rows of one expert's pair list, that
+// expert's B matrix).
 template <int MODE>
 __global__ void __launch_bounds__(kGThreads, 2) gemm_kernel(GemmArgs g) {
-  constexpr bool kGateUp = MODE == kSharedGateUp;
+  constexpr bool kGateUp = MODE == kSharedGateUp || MODE == kBf16GateUp;
+  constexpr bool kRouted = MODE == kBf16GateUp || MODE == kBf16Down;
   __shared__ __attribute__((aligned(16))) uint16_t As[kStages][kBM * kBK];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[kStages][kBN * kBK];
   __shared__ int rowidx[kBM];  // A row (token or pair) of each tile row, -1 = none
@@ -120,16 +127,63 @@ __global__ void __launch_bounds__(kGThreads, 2) gemm_kernel(GemmArgs g) {
   const int xcd = blockIdx.x % 8, per = nblk / 8;
   const int b = blockIdx.x < per * 8 ? xcd * per + blockIdx.x / 8 : blockIdx.x;
   const int mt = b / ntn, nt = b % ntn;
-  const int m0 = mt * kBM, nrows = min(kBM, g.rows - m0);
-  if (nrows <= 0) return;
+  int m0 = mt * kBM, nrows, expert = 0;
+  if constexpr (kRouted) {
+    // Row tile mt of the routed experts: expert e has ceil(count_e / 256)
+    // row tiles, in expert order; tiles past the last one have no rows.
+    if (wv == 0) {
+      int c4[4], n4[4], tot = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ee = 4 * lane + i;
+        c4[i] = ee < g.E ? g.counts[ee] : 0;
+        n4[i] = (c4[i] + kBM - 1) / kBM;
+        tot += n4[i];
+      }
+      int incl = tot;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int v = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += v;
+      }
+      int before = incl - tot;
+      if (lane == 0) tile_info[0] = -1;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (mt >= before && mt < before + n4[i]) {
+          const int q = mt - before;
+          tile_info[0] = 4 * lane + i;
+          tile_info[1] = q * kBM;
+          tile_info[2] = min(kBM, c4[i] - q * kBM);
+        }
+        before += n4[i];
+      }
+    }
+    __syncthreads();
+    expert = tile_info[0];
+    if (expert < 0) return;
+    m0 = tile_info[1];
+    nrows = tile_info[2];
+  } else {
+    nrows = min(kBM, g.rows - m0);
+    if (nrows <= 0) return;
+  }
   const int n0 = nt * (kGateUp ? kBN / 2 : kBN);
 
   // Row indices of the tile; rows past the end repeat the first row (their
   // loads stay in bounds and their results are dropped).
   for (int i = threadIdx.x; i < kBM; i += kGThreads) {
-    const int src = m0 + (i < nrows ? i : 0);
-    rowidx[i] = src;
-    outrow[i] = i < nrows ? src : -1;
+    if constexpr (kRouted) {
+      const int p = g.lists[(size_t)expert * g.list_stride + m0 + (i < nrows ? i : 0)];
+      rowidx[i] = kGateUp ? p / g.top_k : p;
+      outrow[i] = i < nrows ? p : -1;
+    } else {
+      const int src = m0 + (i < nrows ? i : 0);
+      rowidx[i] = src;
+      outrow[i] = i < nrows ? src : -1;
+    }
   }
   __syncthreads();
 
@@ -173,7 +227,8 @@ __global__ void __launch_bounds__(kGThreads, 2) gemm_kernel(GemmArgs g) {
     b_slot[u] = sl;
   }
   const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(g.a, (size_t)g.a_rows * K * 2);
-  const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(g.b, (size_t)ncols_b * K * 2);
+  const __amdgpu_buffer_rsrc_t rs_b =
+      make_rsrc(g.b + (size_t)expert * ncols_b * K * 2, (size_t)ncols_b * K * 2);
 
   struct Regs {
     u32x4_t a[4];
@@ -277,7 +332,7 @@ __global__ void __launch_bounds__(kGThreads, 2) gemm_kernel(GemmArgs g) {
           const int col = n0 + 32 * n + cl;
           g.c[(size_t)orow * g.ldc + col] = (uint16_t)f32_to_bf16(swiglu(acc[m][n][r], acc[m][n + 2][r]));
         }
-      } else {  // kSharedDown
+      } else {  // kSharedDown, kBf16Down
 #pragma unroll
         for (int n = 0; n < 4; ++n)
           g.c[(size_t)orow * g.ldc + n0 + 32 * n + cl] = (uint16_t)f32_to_bf16(acc[m][n][r]);
@@ -979,7 +1034,41 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
   // 4. routed gate/up: row tiles bounded by sum_e ceil(count_e / 256)
   if ((err = mark(3)) != hipSuccess) return err;
   const int max_row_tiles = (P + kRBM - 1) / kRBM + E;
-  {
+  if (a.bw13) {
+    // BF16 experts: gemm_kernel on the pair lists (the row tiles of every
+    // expert, in expert order; blocks past the last tile exit at once)
+    GemmArgs gu{};
+    gu.a = a.x;
+    gu.a_rows = M;
+    gu.b = reinterpret_cast<const uint8_t *>(a.bw13);
+    gu.c = a.act;
+    gu.K = H;
+    gu.ncols = I;
+    gu.ldc = I;
+    gu.I = I;
+    gu.top_k = k;
+    gu.lists = a.lists;
+    gu.counts = a.counts;
+    gu.list_stride = M;
+    gu.E = E;
+    if ((err = launch_gemm<kBf16GateUp>(gu, max_row_tiles, I / (kBN / 2), st)) != hipSuccess) return err;
+    // 5. routed down
+    if ((err = mark(4)) != hipSuccess) return err;
+    GemmArgs dn{};
+    dn.a = a.act;
+    dn.a_rows = P;
+    dn.b = reinterpret_cast<const uint8_t *>(a.bw2);
+    dn.c = a.y;
+    dn.K = I;
+    dn.ncols = H;
+    dn.ldc = H;
+    dn.top_k = k;
+    dn.lists = a.lists;
+    dn.counts = a.counts;
+    dn.list_stride = M;
+    dn.E = E;
+    if ((err = launch_gemm<kBf16Down>(dn, max_row_tiles, H / kBN, st)) != hipSuccess) return err;
+  } else {
     GemmArgs gu{};
     gu.a = a.x;
     gu.a_rows = M;
@@ -997,10 +1086,8 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
     gu.list_stride = M;
     gu.E = E;
     if ((err = launch_routed<kRoutedGateUp>(gu, max_row_tiles, st)) != hipSuccess) return err;
-  }
-  // 5. routed down
-  if ((err = mark(4)) != hipSuccess) return err;
-  {
+    // 5. routed down
+    if ((err = mark(4)) != hipSuccess) return err;
     GemmArgs dn{};
     dn.a = a.act;
     dn.a_rows = P;

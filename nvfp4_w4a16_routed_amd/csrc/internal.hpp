@@ -16,6 +16,9 @@ constexpr int kRouteExperts = 4;
 constexpr int kMaxDecodePairs = 512;
 constexpr int kMaxExperts = 256;
 constexpr int kMaxDecodeM = 64;
+// Bytes of x the decode kernel stages in each block's LDS (all of x when
+// M * H * 2 fits; the fused residual add + RMS norm needs that).
+constexpr int kDecodeXStage = 65536;
 // Decode kernel grid limits: blocks, routing blocks, and the blocks of its
 // shared gate/up and shared down segments.
 constexpr int kMaxDecodeBlocks = 1024;
@@ -50,6 +53,11 @@ struct DecodeArgs {
   const uint8_t *ssgu, *ssdown; // NVFP4 shared expert: block scales (NULL: bf16 shared)
   const float *asgu, *asdown;   // NVFP4 shared expert: device global scales
   const uint16_t *sh_ext;       // precomputed shared output [M, H] (then sgu is NULL)
+  // residual add + RMS norm formed inside the kernel (NULL ln_a: x given);
+  // needs M * H * 2 <= kDecodeXStage
+  const uint16_t *ln_a, *ln_r, *ln_w;
+  float eps;
+  uint16_t *res_out, *xn_out;
   const int32_t *ids_in;        // forced routing, NULL = route
   const float *tw_in;
   uint16_t *logits;
@@ -130,10 +138,11 @@ hipError_t launch_take_wait_errors(DecodeSync *sync, int32_t *out, hipStream_t s
 // Arguments of the grouped (prefill) path: device pointers, caller-owned.
 struct GroupedArgs {
   const uint16_t *x, *router;
-  const uint8_t *w13, *s13;
+  const uint8_t *w13, *s13;     // NVFP4 routed experts (NULL with BF16 experts)
   const float *a13;
   const uint8_t *w2, *s2;
   const float *a2;
+  const uint16_t *bw13, *bw2;   // BF16 routed experts [E, 2I, H], [E, H, I] (else NULL)
   const uint16_t *sgu, *sdown;  // shared expert (bf16), NULL = none
   const uint16_t *sh_ext;       // precomputed shared output [M, H] (then sgu is NULL), or NULL
   void *sh_ready;               // hipEvent_t completing sh_ext, or NULL

@@ -124,7 +124,8 @@ def run_block(binding, inp: dict, path: str = "decode", forced=None, want_debug=
     x = d["x"]
     out = torch.empty((M, H), dtype=torch.int16, device="cuda")
     fn = {"decode": binding.flint_moe_decode, "grouped": binding.flint_moe_grouped,
-          "bf16_decode": binding.flint_moe_bf16_decode}[path]
+          "bf16_decode": binding.flint_moe_bf16_decode,
+          "bf16_grouped": binding.flint_moe_bf16_grouped}[path]
     fn(x, d["router"], experts_of(d), shared_of(d), k, ws, out=out, debug=dbg)
     torch.cuda.synchronize()
     r = dict(out=host(out))

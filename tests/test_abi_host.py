@@ -199,3 +199,19 @@ def test_decode_noalloc_rejects_bad_arguments():
     assert _noalloc(x=MIS) == -3
     assert _noalloc(shared=fm.SharedExpert(A, A, 700)) == -2
     assert _noalloc(M=0, x=None) == 0
+
+
+def test_bf16_grouped_rejects_bad_arguments():
+    L = fm.lib()
+
+    def call(w, M=8, H=2048, I=768, k=8, shared=None, ws_bytes=1 << 62):
+        return L.flint_moe_bf16_grouped(A, A, ctypes.byref(w), ctypes.byref(shared) if shared else None,
+                                        M, H, 128, I, k, A, None, A, ws_bytes, None)
+
+    assert call(fm.Bf16Experts(A, None)) == -1
+    assert call(fm.Bf16Experts(MIS, A)) == -3
+    assert call(fm.Bf16Experts(A, A), H=1000) == -2
+    assert call(fm.Bf16Experts(A, A), M=174763) == -2         # act past 2^31 bytes
+    assert call(fm.Bf16Experts(A, A), shared=fm.SharedExpert(A, A, 0)) == -2
+    assert call(fm.Bf16Experts(A, A), ws_bytes=10) == -4
+    assert call(fm.Bf16Experts(None, None), M=0) == 0
