@@ -150,6 +150,26 @@ def zipf_router(seed: int, x_bits: np.ndarray, E: int, s: float = 1.1) -> np.nda
     return to_bf16_bits(Rt.T.copy())
 
 
+_MEMO: dict = {}
+
+
+def _experts_memo(seed: int, kind: str, E: int, Hh: int, Ii: int) -> dict:
+    """The routed experts of a workload (NVFP4 or BF16), kept for the last two
+    keys so workloads that differ only in M share one draw (callers must not
+    write into the arrays)."""
+    key = (seed, kind, E, Hh, Ii)
+    if key not in _MEMO:
+        if kind == "nvfp4":
+            w = nvfp4_experts(seed, E, Hh, Ii)
+        else:
+            w = dict(bw13=bf16_normal(seed, T_BW13, (E, 2 * Ii, Hh), 0.02),
+                     bw2=bf16_normal(seed, T_BW2, (E, Hh, Ii), 0.02))
+        while len(_MEMO) >= 2:
+            _MEMO.pop(next(iter(_MEMO)))
+        _MEMO[key] = w
+    return dict(_MEMO[key])
+
+
 def make_inputs(cfg: dict | int, seed: int | None = None, M: int | None = None,
                 with_shared: bool = True) -> dict:
     """All inputs of one workload as numpy arrays of storage bits.
@@ -172,11 +192,7 @@ def make_inputs(cfg: dict | int, seed: int | None = None, M: int | None = None,
     else:
         router = bf16_normal(seed, T_ROUTER, (E, Hh), 0.02)
     d = dict(cfg=dict(cfg, M=M), seed=seed, x=x, router=router)
-    if cfg["experts"] == "nvfp4":
-        d.update(nvfp4_experts(seed, E, Hh, Ii))
-    else:
-        d["bw13"] = bf16_normal(seed, T_BW13, (E, 2 * Ii, Hh), 0.02)
-        d["bw2"] = bf16_normal(seed, T_BW2, (E, Hh, Ii), 0.02)
+    d.update(_experts_memo(seed, cfg["experts"], E, Hh, Ii))
     if with_shared and SIi > 0:
         d["sgu"] = bf16_normal(seed, T_SGU, (2 * SIi, Hh), 0.02)
         d["sdown"] = bf16_normal(seed, T_SDOWN, (Hh, SIi), 0.02)
