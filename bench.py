@@ -53,6 +53,8 @@ def _args():
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline workload (for profiling its kernel)")
     ap.add_argument("--no-grouped", action="store_true", help="skip the M=4096 grouped lines")
+    ap.add_argument("--grouped-only", action="store_true",
+                    help="time only the M=4096 NVFP4 grouped line (for profiling its kernels)")
     ap.add_argument("--grouped-steps", type=int, default=30)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain fp32 copy of MIB MiB 5 times (HBM counter scale)")
@@ -417,6 +419,12 @@ def main():
     import synth
 
     fm.lib()
+    if a.grouped_only:
+        wg = Workload(fm, synth, torch, 4, "grouped", 2)
+        msg = wg.time_steps(a.grouped_steps, 3)
+        print(json.dumps({"grouped": grouped_entry(wg, msg, wg.time_stages(a.grouped_steps), fm)}),
+              flush=True)
+        return
     cfg_idx = a.config
     path = "bf16_decode" if synth.CONFIGS[cfg_idx]["experts"] == "bf16" else "decode"
     w = Workload(fm, synth, torch, cfg_idx, path, a.layers)

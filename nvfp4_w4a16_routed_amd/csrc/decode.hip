@@ -132,6 +132,11 @@ __shared__ long long g_trace_lds[kWaves * 16];
   do {                                                                        \
     if (lane_id() == 0) g_trace_lds[wave_id() * 16 + (slot)] = __builtin_amdgcn_s_memrealtime(); \
   } while (0)
+#define TRACE_FIRST(P, slot)                                                  \
+  do {                                                                        \
+    if (lane_id() == 0 && g_trace_lds[wave_id() * 16 + (slot)] == 0)           \
+      g_trace_lds[wave_id() * 16 + (slot)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
 #define TRACE_INIT()                                                          \
   do {                                                                        \
     if (lane_id() < 16) g_trace_lds[wave_id() * 16 + lane_id()] = 0;          \
@@ -145,6 +150,9 @@ __shared__ long long g_trace_lds[kWaves * 16];
 #else
 #define TRACE(P, slot) \
   do {                 \
+  } while (0)
+#define TRACE_FIRST(P, slot) \
+  do {                       \
   } while (0)
 #define TRACE_INIT() \
   do {               \
@@ -1144,6 +1152,7 @@ decode_kernel(Params P) {
         wave_wait_flags(S->gb, owner_block(R, R.cum_gu, s, 0, QB, P.nb),
                         owner_block(R, R.cum_gu, s, Gm::N_GU - 1, QB, P.nb) + 1, P.seq, P.polls, S,
                         kWaitGateUp);
+        TRACE_FIRST(P, 10);
         if (nx > 0) wait_lds_at_least(&R.done_b, kWaves, S);
         for (int j = 0; j < nc + nx; ++j)  // every row's copies in flight at once
           issue_copy_to_lds<true>(j < nc ? slice + (size_t)j * I : xpart + (size_t)(j - nc) * I,
@@ -1152,6 +1161,7 @@ decode_kernel(Params P) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        TRACE_FIRST(P, 12);
       }
       for (int j = 0; j < nc; ++j)
         down_one<FMT, H, I, kSrcLds>(st.w, slice + (size_t)j * I, st.alpha, j, ob);
