@@ -667,15 +667,23 @@ __global__ void __launch_bounds__(kGThreads, 1) routed_gemm_kernel(GemmArgs g) {
 // k = 16 sub + 8 (l / 32) + 0..7 for sub-step sub).  The MFMA forms tiles
 // with experts as rows: lane l holds token l % 32.
 constexpr int kRouterTokens = 32;
+// Experts per router block: one 32-expert tile, so a prefill batch fills
+// the chip with (M / 32) x (E / 32) blocks.
+constexpr int kRouterExperts = 32;
 
+// (counts, may be NULL: E words zeroed by block (0, 0) for the pair lists
+// that the top-k kernel builds next)
 __global__ void __launch_bounds__(kGThreads, 1) router_kernel(const uint16_t *__restrict__ x,
                                                               const uint16_t *__restrict__ R, int M, int K,
-                                                              int E, uint16_t *__restrict__ logits) {
+                                                              int E, uint16_t *__restrict__ logits,
+                                                              int32_t *__restrict__ counts) {
   __shared__ f32x16_t part[3][4][kWave];  // partial tiles of waves 1..3
   const int lane = lane_id(), wv = wave_id(), h = lane >> 5, r = lane & 31;
+  if (counts && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = threadIdx.x; i < E; i += kGThreads) counts[i] = 0;
   const int t0 = blockIdx.x * kRouterTokens;
-  const int e0 = blockIdx.y * 128;
-  const int nte = min(4, (E - e0 + 31) / 32);
+  const int e0 = blockIdx.y * kRouterExperts;
+  const int nte = min(kRouterExperts / 32, (E - e0 + 31) / 32);
   const __amdgpu_buffer_rsrc_t rs_x = make_rsrc(x, (size_t)M * K * 2);
   const __amdgpu_buffer_rsrc_t rs_r = make_rsrc(R, (size_t)E * K * 2);
   // this wave's K range: chunks of 64 [c0, c1) (K is a multiple of 64)
@@ -753,9 +761,8 @@ __global__ void __launch_bounds__(kGThreads, 1) router_kernel(const uint16_t *__
         }
     }
   };
-  if (nte <= 1) run(IC<1>{});
-  else if (nte <= 2) run(IC<2>{});
-  else run(IC<4>{});
+  (void)nte;  // every block holds one 32-expert tile (rows past E are clamped)
+  run(IC<kRouterExperts / 32>{});
 }
 
 // out[t, h] = bf16(bf16(sum_j tw[t, j] y[t*k + j, h]) + sh[t, h]) for 8
@@ -775,11 +782,13 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint16_t *__restrict
   for (int j0 = 0; j0 < k; j0 += 8) {
     u32x4_t v[8];
     float w[8];
+    // every y row is loaded at once, independent of the ids (a dropped id
+    // gets weight 0; rows past k repeat the last pair's row)
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int j = j0 + u;
-      const bool on = j < k && (unsigned)ids[(size_t)t * k + j] < (unsigned)E;
-      v[u] = on ? load16(y + ((size_t)t * k + j) * H + h) : u32x4_t{0, 0, 0, 0};
+      const int j = j0 + u < k ? j0 + u : k - 1;
+      v[u] = load16(y + ((size_t)t * k + j) * H + h);
+      const bool on = j0 + u < k && (unsigned)ids[(size_t)t * k + j] < (unsigned)E;
       w[u] = on ? tw[(size_t)t * k + j] : 0.0f;
     }
 #pragma unroll
@@ -933,9 +942,9 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
   // 1. router logits and top-k (skipped with forced routing)
   if ((err = mark(0)) != hipSuccess) return err;
   if (!a.ids_in) {
-    hipLaunchKernelGGL(router_kernel, dim3((M + kRouterTokens - 1) / kRouterTokens, (E + 127) / 128),
-                       dim3(kGThreads), 0, st,
-                       a.x, a.router, M, H, E, a.logits);
+    hipLaunchKernelGGL(router_kernel,
+                       dim3((M + kRouterTokens - 1) / kRouterTokens, (E + kRouterExperts - 1) / kRouterExperts),
+                       dim3(kGThreads), 0, st, a.x, a.router, M, H, E, a.logits, nullptr);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if ((err = launch_topk(a.logits, M, E, k, a.ids, a.tw, nullptr, st)) != hipSuccess) return err;
   }
