@@ -671,16 +671,11 @@ constexpr int kRouterTokens = 32;
 // the chip with (M / 32) x (E / 32) blocks.
 constexpr int kRouterExperts = 32;
 
-// (counts, may be NULL: E words zeroed by block (0, 0) for the pair lists
-// that the top-k kernel builds next)
 __global__ void __launch_bounds__(kGThreads, 1) router_kernel(const uint16_t *__restrict__ x,
                                                               const uint16_t *__restrict__ R, int M, int K,
-                                                              int E, uint16_t *__restrict__ logits,
-                                                              int32_t *__restrict__ counts) {
+                                                              int E, uint16_t *__restrict__ logits) {
   __shared__ f32x16_t part[3][4][kWave];  // partial tiles of waves 1..3
   const int lane = lane_id(), wv = wave_id(), h = lane >> 5, r = lane & 31;
-  if (counts && blockIdx.x == 0 && blockIdx.y == 0)
-    for (int i = threadIdx.x; i < E; i += kGThreads) counts[i] = 0;
   const int t0 = blockIdx.x * kRouterTokens;
   const int e0 = blockIdx.y * kRouterExperts;
   const int nte = min(kRouterExperts / 32, (E - e0 + 31) / 32);
@@ -944,7 +939,7 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
   if (!a.ids_in) {
     hipLaunchKernelGGL(router_kernel,
                        dim3((M + kRouterTokens - 1) / kRouterTokens, (E + kRouterExperts - 1) / kRouterExperts),
-                       dim3(kGThreads), 0, st, a.x, a.router, M, H, E, a.logits, nullptr);
+                       dim3(kGThreads), 0, st, a.x, a.router, M, H, E, a.logits);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if ((err = launch_topk(a.logits, M, E, k, a.ids, a.tw, nullptr, st)) != hipSuccess) return err;
   }

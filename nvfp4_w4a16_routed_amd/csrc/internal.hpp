@@ -112,11 +112,8 @@ Workspace carve_workspace(void *base, int M, int H, int E, int I, int SI, int to
 hipError_t launch_dequant(const uint8_t *w, const uint8_t *s, int rows, int K,
                           uint16_t *out, hipStream_t st);
 
-// lists / counts (both or neither): the per-expert pair lists [E, M] built
-// as the ids are chosen; counts [E] must be zero before the launch.
 hipError_t launch_topk(const uint16_t *logits, int M, int E, int top_k, int32_t *ids,
-                       float *tw, float *scores, hipStream_t st, int32_t *lists = nullptr,
-                       int32_t *counts = nullptr);
+                       float *tw, float *scores, hipStream_t st);
 
 // Router logits + top-k (+ routing plan when `plan` is non-NULL).
 hipError_t launch_route(const uint16_t *x, const uint16_t *router, int M, int H, int E,

@@ -30,14 +30,9 @@ constexpr int kThreads = 256;  // 4 waves
 
 // Top-k of one token's logits by one wave (top_k <= E <= 256).  Selection j
 // is kept in a register of lane j % 64 (slot j / 64).  Writes the ids, tw
-// and (if non-NULL) scores rows of the token.  lists (may be NULL): each
-// selected expert e also gets pair p0 + j appended to its list
-// lists[e * stride ...] through the arrival counter counts[e] (the order
-// inside a list is the order of arrival; the consumers' results do not
-// depend on it).
+// and (if non-NULL) scores rows of the token.
 __device__ void topk_token(const uint16_t *lrow, int E, int top_k, int32_t *ids, float *tw,
-                           float *scores, int32_t *lists = nullptr, int stride = 0,
-                           int32_t *counts = nullptr, int p0 = 0) {
+                           float *scores) {
   const int lane = threadIdx.x & (kWave - 1);
   int keys[4], sel[4] = {kNoKey, kNoKey, kNoKey, kNoKey};
 #pragma unroll
@@ -70,11 +65,9 @@ __device__ void topk_token(const uint16_t *lrow, int E, int top_k, int32_t *ids,
   for (int i = 0; i < 4; ++i) {
     const int j = kWave * i + lane;
     if (j < top_k) {
-      const int e = key_expert(sel[i]);
-      ids[j] = e;
+      ids[j] = key_expert(sel[i]);
       tw[j] = round_bf16(s[i] / D);
       if (scores) scores[j] = s[i];
-      if (lists) lists[(size_t)e * stride + atomicAdd(&counts[e], 1)] = p0 + j;
     }
   }
 }
@@ -215,17 +208,14 @@ route_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ router
 }
 
 // Top-k of given logits: one wave per token, 4 tokens per block.
-// (lists != NULL: also the per-expert pair lists, counts zeroed beforehand)
 __global__ void __launch_bounds__(kThreads)
 topk_kernel(const uint16_t *__restrict__ logits, int M, int E, int top_k,
-            int32_t *__restrict__ ids, float *__restrict__ tw, float *__restrict__ scores,
-            int32_t *__restrict__ lists, int32_t *__restrict__ counts) {
+            int32_t *__restrict__ ids, float *__restrict__ tw, float *__restrict__ scores) {
   const int wv = threadIdx.x / kWave;
   const int t = blockIdx.x * 4 + wv;
   if (t >= M) return;
   topk_token(logits + (size_t)t * E, E, top_k, ids + (size_t)t * top_k,
-             tw + (size_t)t * top_k, scores ? scores + (size_t)t * top_k : nullptr, lists, M,
-             counts, t * top_k);
+             tw + (size_t)t * top_k, scores ? scores + (size_t)t * top_k : nullptr);
 }
 
 __global__ void __launch_bounds__(kThreads)
@@ -238,11 +228,10 @@ plan_kernel(const int32_t *__restrict__ ids, int M, int E, int top_k, Plan plan)
 }  // namespace
 
 hipError_t launch_topk(const uint16_t *logits, int M, int E, int top_k, int32_t *ids,
-                       float *tw, float *scores, hipStream_t st, int32_t *lists,
-                       int32_t *counts) {
+                       float *tw, float *scores, hipStream_t st) {
   dim3 grid((M + 3) / 4);
   hipLaunchKernelGGL(topk_kernel, grid, dim3(kThreads), 0, st, logits, M, E, top_k, ids,
-                     tw, scores, lists, counts);
+                     tw, scores);
   return hipGetLastError();
 }
 
