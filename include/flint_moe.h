@@ -99,9 +99,10 @@ typedef struct {
  * shared expert (w_gu, w_down and SI are ignored) and adds sh_in [M, H]
  * bf16 (16-byte aligned) in its place, out = bf16(bf16(routed) + sh_in);
  * sh_ready, a hipEvent_t or NULL, is waited on by the call's stream before
- * sh_in is read (decode entry points: before the block's one kernel starts,
- * whose combine reads it; flint_moe_grouped: before its combine kernel), so
- * the producer may still be running when the call is made. */
+ * sh_in is read (decode entry points up to 16 tokens: before the block's one
+ * kernel starts, whose combine reads it; flint_moe_grouped and the decode
+ * entry points past 16 tokens: before the combine kernel), so the producer
+ * may still be running when the call is made. */
 typedef struct {
   const uint16_t *w_gu;   /* [2*SI, H] bf16, rows 0..SI-1 gate, SI..2SI-1 up */
   const uint16_t *w_down; /* [H, SI] bf16 */
@@ -138,8 +139,9 @@ typedef struct {
    * hipEventElapsedTime(events[i], events[i + 1]) times stage i.  Stages of
    * flint_moe_grouped: 0 router GEMM and top-k, 1 expert pair lists,
    * 2 shared gate/up, 3 routed gate/up, 4 routed down, 5 shared down,
-   * 6 combine.  The decode entry points run one kernel: it is stage 0 and
-   * the other stages take no time. */
+   * 6 combine.  The decode entry points run one kernel up to 16 tokens (it
+   * is stage 0 and the other stages take no time) and these stages past 16
+   * tokens. */
   void **stage_events;
   /* Decode entry points only (test hooks of the bounded waits; 0 = off):
    * wait_polls > 0 caps every cross-block wait of the decode kernel at that
@@ -214,7 +216,11 @@ int flint_moe_wait_errors(void *ws, size_t ws_bytes, int32_t *errors, void *stre
 
 /* The MoE block on NVFP4 experts for decode-size batches, 1 <= M <= 64
  * (page "vllm.models.flint.ops.moe", flint_moe, decode branch):
- * out [M, H] bf16. */
+ * out [M, H] bf16.  Up to 16 tokens the whole block is one kernel (per-token
+ * dot products over the touched experts' weights); past 16 tokens, where
+ * each expert's weights serve several tokens, it runs the chain of
+ * flint_moe_grouped with matrix-core GEMMs that stream each touched
+ * expert's weights once (the same rounding rule either way). */
 int flint_moe_decode(const uint16_t *x, const uint16_t *router,
                      const flint_nvfp4_experts *w, const flint_shared_expert *shared,
                      int M, int H, int E, int I, int top_k, uint16_t *out,
@@ -228,7 +234,8 @@ int flint_moe_decode(const uint16_t *x, const uint16_t *router,
  * 4 MiB array inside the library, one per GPU, kept until the process
  * ends; sizes whose workspace would exceed it (flint_moe_workspace_bytes)
  * return FLINT_ERR_WORKSPACE (every size the decode entry points accept
- * fits).  Every call on a GPU shares that GPU's scratch: calls are ordered
+ * fits).  Past 16 tokens the shared expert runs on `stream` itself (no
+ * second stream).  Every call on a GPU shares that GPU's scratch: calls are ordered
  * by the library's per-device launch chain, but two calls must not be
  * queued concurrently from different host threads with debug outputs that
  * alias.  Nothing in the scratch needs clearing between calls (its flags

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libflint_moe.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["abi.cpp", "route.hip", "decode.hip", "dequant.hip", "grouped.hip", "norm.hip"]
+SOURCES = ["abi.cpp", "route.hip", "decode.hip", "dequant.hip", "grouped.hip", "norm.hip", "skinny.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -140,6 +140,17 @@ struct NormIn {
   uint16_t *res, *xn;
 };
 
+int run_grouped(GroupedArgs a, bool have_w, const uint16_t *x, const uint16_t *router,
+                const flint_shared_expert *shared, int M, int H, int E, int I, int top_k,
+                uint16_t *out, const flint_moe_debug *dbg, void *ws, size_t ws_bytes,
+                void *stream);
+
+// The decode kernel runs batches up to this many tokens; larger ones run
+// the chain of the grouped path with its skinny expert GEMMs (at that size
+// each expert's weights serve many tokens, which the decode kernel's
+// per-token dot products cannot reuse).
+constexpr int kDecodeKernelMaxM = 16;
+
 // The decode pipeline shared by the NVFP4 and BF16 experts (norm: the
 // residual add + RMS norm in front, formed inside the kernel; x is then
 // norm->xn, written by the kernel).
@@ -147,13 +158,30 @@ int run_decode(int fmt, const uint16_t *x, const uint16_t *router, const void *w
                const uint8_t *s13, const float *a13, const void *w2, const uint8_t *s2,
                const float *a2, const flint_shared_expert *shared, int M, int H, int E, int I,
                int top_k, uint16_t *out, const flint_moe_debug *dbg, void *ws,
-               size_t ws_bytes, hipStream_t st, const NormIn *norm = nullptr) {
+               size_t ws_bytes, hipStream_t st, const NormIn *norm = nullptr,
+               bool no_side_stream = false) {
   const bool ext_sh = shared && shared->sh_in;  // precomputed shared output
   const bool has_shared = !ext_sh && shared && shared->w_gu;
   const int SI = has_shared ? shared->SI : 0;
   Workspace W = carve_workspace(ws, M, H, E, I, SI, top_k);
   if (W.bytes > ws_bytes) return FLINT_ERR_WORKSPACE;
   if (M == 0) return FLINT_OK;
+  if (M > kDecodeKernelMaxM && !norm && grouped_shape_supported(H, I, SI)) {
+    GroupedArgs ga{};
+    if (fmt == kNvfp4) {
+      ga.w13 = static_cast<const uint8_t *>(w13);
+      ga.s13 = s13;
+      ga.a13 = a13;
+      ga.w2 = static_cast<const uint8_t *>(w2);
+      ga.s2 = s2;
+      ga.a2 = a2;
+    } else {
+      ga.bw13 = static_cast<const uint16_t *>(w13);
+      ga.bw2 = static_cast<const uint16_t *>(w2);
+    }
+    ga.inline_shared = no_side_stream;
+    return run_grouped(ga, true, x, router, shared, M, H, E, I, top_k, out, dbg, ws, ws_bytes, st);
+  }
 
   const bool forced = dbg && dbg->ids_in;
   uint16_t *logits = (dbg && dbg->logits_out) ? dbg->logits_out : W.logits;
@@ -443,7 +471,8 @@ int flint_moe_decode_noalloc(const uint16_t *x, const uint16_t *router,
   void *ws = nullptr;
   if (hipError_t e = scratch_ptr(&ws); e != hipSuccess) return hip_status(e);
   return run_decode(kNvfp4, x, router, w->w13, w->s13, w->a13, w->w2, w->s2, w->a2, shared, M,
-                    H, E, I, top_k, out, dbg, ws, kScratchBytes, (hipStream_t)stream);
+                    H, E, I, top_k, out, dbg, ws, kScratchBytes, (hipStream_t)stream, nullptr,
+                    /*no_side_stream=*/true);
 }
 
 int flint_moe_ll(const uint16_t *attn_out, const uint16_t *residual, const uint16_t *ln_weight,
@@ -473,7 +502,7 @@ int flint_moe_ll(const uint16_t *attn_out, const uint16_t *residual, const uint1
       !aligned16(w->a2))
     return FLINT_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
-  if ((long)M * H * 2 <= kDecodeXStage) {
+  if ((long)M * H * 2 <= kDecodeXStage && M <= kDecodeKernelMaxM) {
     // every block of the decode kernel forms the normed rows itself (they
     // fit its LDS): one launch
     const NormIn norm{attn_out, residual, ln_weight, eps, residual_out, xn_out};

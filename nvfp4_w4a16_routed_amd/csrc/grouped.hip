@@ -950,7 +950,37 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
   // 3. shared gate/up (and 6. shared down): on the side stream unless
   // stage events are asked for
   if ((err = mark(2)) != hipSuccess) return err;
-  const bool side = a.sgu && !a.events;
+  const bool side = a.sgu && !a.events && !a.inline_shared;
+  // Few tokens (decode-size batches): every expert GEMM on the skinny
+  // kernels, whose waves each stream their own weight rows.
+  const bool sk = M <= kSkinnyMaxM && skinny_shape_supported(H, I, true) &&
+                  skinny_shape_supported(I, H, false) &&
+                  (!a.sgu || (skinny_shape_supported(H, SI, true) && skinny_shape_supported(SI, H, false)));
+  auto sk_launch = [&](const uint16_t *A, int a_rows, const void *w, const uint8_t *ws,
+                       const float *alpha, uint16_t *c, int c_rows, const int32_t *lists,
+                       const int32_t *counts, int E_, int K, int wrows, int ncols, bool gate_up,
+                       int wfmt, hipStream_t s) -> hipError_t {
+    SkinnyArgs g{};
+    g.a = A;
+    g.a_rows = a_rows;
+    g.w = static_cast<const uint8_t *>(w);
+    g.ws = ws;
+    g.alpha = alpha;
+    g.c = c;
+    g.c_rows = c_rows;
+    g.lists = lists;
+    g.counts = counts;
+    g.list_stride = M;
+    g.top_k = k;
+    g.nrows = M;
+    g.K = K;
+    g.wrows = wrows;
+    g.ncols = ncols;
+    g.ldc = ncols;
+    g.I = ncols;
+    g.E = E_;
+    return launch_skinny(g, gate_up, wfmt, s);
+  };
   hipStream_t sst = st;
   std::unique_lock<std::mutex> side_lock;
   SideStream *sd = nullptr;
@@ -997,6 +1027,9 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
     return launch_routed<kRoutedDown>(g, (M + kRBM - 1) / kRBM + 1, sst);
   };
   auto shared_down = [&]() -> hipError_t {
+    if (sk)
+      return sk_launch(a.sact, M, a.sdown, a.s_down, a.a_down, a.sh, M, nullptr, nullptr, 1, SI, H,
+                       H, false, a.s_gu ? kNvfp4 : kBf16, sst);
     if (a.s_gu) return nv_shared(kRoutedDown);
     GemmArgs sdn{};
     sdn.a = a.sact;
@@ -1009,7 +1042,15 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
     sdn.ldc = H;
     return launch_gemm<kSharedDown>(sdn, (M + kBM - 1) / kBM, H / kBN, sst);
   };
-  if (a.sgu && a.s_gu) {
+  if (a.sgu && sk) {
+    if ((err = sk_launch(a.x, M, a.sgu, a.s_gu, a.a_gu, a.sact, M, nullptr, nullptr, 1, H, 2 * SI, SI,
+                         true, a.s_gu ? kNvfp4 : kBf16, sst)) != hipSuccess)
+      return err;
+    if (side) {
+      if ((err = shared_down()) != hipSuccess) return err;
+      if ((err = hipEventRecord(sd->join, sst)) != hipSuccess) return err;
+    }
+  } else if (a.sgu && a.s_gu) {
     hipLaunchKernelGGL(iota_list_kernel, dim3((M + 255) / 256), dim3(256), 0, sst, a.sh_lists, M, a.sh_counts);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if ((err = nv_shared(kRoutedGateUp)) != hipSuccess) return err;
@@ -1038,7 +1079,19 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
   // 4. routed gate/up: row tiles bounded by sum_e ceil(count_e / 256)
   if ((err = mark(3)) != hipSuccess) return err;
   const int max_row_tiles = (P + kRBM - 1) / kRBM + E;
-  if (a.bw13) {
+  if (sk) {
+    const bool bf = a.bw13 != nullptr;
+    if ((err = sk_launch(a.x, M, bf ? (const void *)a.bw13 : (const void *)a.w13, bf ? nullptr : a.s13,
+                         bf ? nullptr : a.a13, a.act, P, a.lists, a.counts, E, H, 2 * I, I, true,
+                         bf ? kBf16 : kNvfp4, st)) != hipSuccess)
+      return err;
+    // 5. routed down
+    if ((err = mark(4)) != hipSuccess) return err;
+    if ((err = sk_launch(a.act, P, bf ? (const void *)a.bw2 : (const void *)a.w2, bf ? nullptr : a.s2,
+                         bf ? nullptr : a.a2, a.y, P, a.lists, a.counts, E, I, H, H, false,
+                         bf ? kBf16 : kNvfp4, st)) != hipSuccess)
+      return err;
+  } else if (a.bw13) {
     // BF16 experts: gemm_kernel on the pair lists (the row tiles of every
     // expert, in expert order; blocks past the last tile exit at once)
     GemmArgs gu{};

@@ -158,8 +158,36 @@ struct GroupedArgs {
   int32_t *counts;              // [E]
   uint16_t *act, *y, *sact, *sh, *out;
   void **events;                // NULL, or 8 hipEvent_t: recorded before each stage and at the end
+  bool inline_shared;           // the shared expert on the caller's stream (no side stream)
   int M, H, E, I, SI, top_k;
 };
+
+// Batches up to this many tokens run the expert GEMMs on the skinny kernels.
+constexpr int kSkinnyMaxM = 64;
+
+// Expert GEMMs with few rows per expert (skinny.hip): what one launch
+// computes (device pointers).
+struct SkinnyArgs {
+  const uint16_t *a;      // A rows [a_rows, K] bf16
+  const uint8_t *w;       // weights [E][wrows][K] bf16, or E2M1 codes [E][wrows][K / 2]
+  const uint8_t *ws;      // E4M3 block scales [E][wrows][K / 16] (NVFP4), else NULL
+  const float *alpha;     // per-expert global scales [E] (NVFP4), else NULL
+  uint16_t *c;            // output rows [c_rows, ldc]
+  const int32_t *lists;   // [E][list_stride] pair indices of each expert (NULL: rows 0 .. nrows - 1)
+  const int32_t *counts;  // [E]
+  int list_stride, top_k;
+  int nrows;              // without lists: the rows (tokens)
+  int a_rows, c_rows;     // extents of A and C (rows)
+  int K, wrows;           // reduction length; weight rows per expert
+  int ncols, ldc, I;      // output columns; output row length; gate/up: offset of the up rows
+  int E;
+};
+
+// gate_up: c[row, n] = bf16(swiglu(alpha a . W[n], alpha a . W[I + n])), n < ncols;
+// else c[row, h] = bf16(alpha a . W[h]).  A row of list entry p: p / top_k
+// (gate/up) or p (down); output row p.  wfmt: kNvfp4 or kBf16.
+hipError_t launch_skinny(const SkinnyArgs &g, bool gate_up, int wfmt, hipStream_t st);
+bool skinny_shape_supported(int K, int ncols, bool gate_up);
 
 // The MoE block with grouped MFMA GEMMs (any M >= 1).
 hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st);

@@ -27,7 +27,7 @@ def _binding():
     yield
 
 
-@pytest.mark.parametrize("M,H,SI", [(300, 512, 256), (37, 256, 128)])
+@pytest.mark.parametrize("M,H,SI", [(300, 512, 256), (37, 256, 128), (20, 512, 256)])
 def test_grouped_nvfp4_shared_expert(M, H, SI):
     print(f"grouped NVFP4 shared expert M={M} H={H} SI={SI}", flush=True)
     inp = synth.make_small(950 + M, M=M, H=H, E=16, I=SI, SI=0, top_k=4, router_std=0.3)
@@ -100,7 +100,9 @@ def _check_nv_shared_run(inp, shw, r, label):
 
 @pytest.mark.parametrize("path,M,H,I,E,k", [("decode", 8, 2048, 768, 128, 8),
                                             ("decode", 5, 256, 128, 16, 4),
-                                            ("noalloc", 3, 512, 256, 32, 8)])
+                                            ("noalloc", 3, 512, 256, 32, 8),
+                                            ("decode", 24, 512, 256, 16, 4),    # skinny GEMMs, side stream
+                                            ("noalloc", 20, 512, 256, 32, 8)])  # skinny GEMMs, inline
 def test_decode_nvfp4_shared_expert(path, M, H, I, E, k):
     print(f"decode NVFP4 shared expert path={path} M={M} H={H} I={I} E={E} k={k}", flush=True)
     inp = synth.make_small(960 + M, M=M, H=H, E=E, I=I, SI=0, top_k=k, router_std=0.3)
