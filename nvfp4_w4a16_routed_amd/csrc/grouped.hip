@@ -760,6 +760,68 @@ __global__ void __launch_bounds__(kGThreads, 1) router_kernel(const uint16_t *__
   run(IC<kRouterExperts / 32>{});
 }
 
+// Router logits of decode-size batches: logits[t, c] = bf16(fp32 x[t] . R[c])
+// for a tile of 16 tokens x 16 experts per block, K split in eighths over
+// the block's eight waves (so a 64-token batch of 128 experts is 32 blocks
+// of 256 lanes each, against 8 blocks of the 32 x 32 tiles above).  Each
+// wave multiplies its K range on v_mfma_f32_16x16x32_bf16 with both
+// operands straight from memory in the MFMA layout (operand lane l: row
+// l % 16, k = 32 s + 8 (l / 16) + 0..7 of step s), eight steps of loads in
+// flight; the eight partial tiles are added in wave order through LDS (a
+// fixed order).  Rows past M or E are clamped to the last row and not
+// stored.  K: a multiple of 256.
+constexpr int kRsWaves = 8;
+constexpr int kRsBatch = 8;  // K steps of 32 per batch of loads
+
+__global__ void __launch_bounds__(kRsWaves * kWave) router_small_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ R, int M, int K, int E,
+    uint16_t *__restrict__ logits) {
+  typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+  __shared__ f32x4_t part[kRsWaves - 1][kWave];
+  const int lane = lane_id(), wv = wave_id(), m = lane & 15, q = lane >> 4;
+  const int t0 = blockIdx.y * 16, e0 = blockIdx.x * 16;
+  const int trow = min(t0 + m, M - 1), erow = min(e0 + m, E - 1);
+  const __amdgpu_buffer_rsrc_t rs_x = make_rsrc(x, (size_t)M * K * 2);
+  const __amdgpu_buffer_rsrc_t rs_r = make_rsrc(R, (size_t)E * K * 2);
+  const int kw = K / kRsWaves;  // this wave's K range [wv kw, wv kw + kw)
+  const uint32_t xo = (uint32_t)trow * (uint32_t)(K * 2) + (uint32_t)(wv * kw + q * 8) * 2;
+  const uint32_t ro = (uint32_t)erow * (uint32_t)(K * 2) + (uint32_t)(wv * kw + q * 8) * 2;
+  const int steps = kw / 32;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < steps; s0 += kRsBatch) {
+    u32x4_t a[kRsBatch], b[kRsBatch];
+#pragma unroll
+    for (int i = 0; i < kRsBatch; ++i) {
+      const uint32_t so = s0 + i < steps ? (uint32_t)(s0 + i) * 64 : kOOB;
+      a[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_r, ro, so, 0));
+      b[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_x, xo, so, 0));
+    }
+#pragma unroll
+    for (int i = 0; i < kRsBatch; ++i)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[i]),
+                                                    __builtin_bit_cast(bf16x8_t, b[i]), acc, 0, 0, 0);
+  }
+  if (wv > 0) part[wv - 1][lane] = acc;
+  __syncthreads();
+  if (wv > 0) return;
+#pragma unroll
+  for (int w = 0; w < kRsWaves - 1; ++w) acc += part[w][lane];
+  // acc[i]: expert e0 + 4 q + i, token t0 + m
+  const int t = t0 + m;
+  if (t < M) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = e0 + 4 * q + i;
+      if (c < E) logits[(size_t)t * E + c] = (uint16_t)f32_to_bf16(acc[i]);
+    }
+  }
+}
+
+bool router_small_supported(int M, int H, int E, int top_k) {
+  return M >= 1 && M <= kSkinnyMaxM && H % (kRsWaves * 32) == 0 && (long)M * top_k <= kMaxDecodePairs &&
+         E <= kMaxExperts;
+}
+
 // out[t, h] = bf16(bf16(sum_j tw[t, j] y[t*k + j, h]) + sh[t, h]) for 8
 // consecutive h per thread: the k rows of y are loaded together (16 bytes
 // each), the sum is exact in fp64 (every product has 16 significant bits)
@@ -934,32 +996,40 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
   auto mark = [&](int i) -> hipError_t {
     return (a.events && a.events[i]) ? hipEventRecord((hipEvent_t)a.events[i], st) : hipSuccess;
   };
-  // 1. router logits and top-k (skipped with forced routing)
+  // Few tokens (decode-size batches): every expert GEMM on the skinny
+  // kernels, whose waves each stream their own weight rows and which find
+  // their rows from the routing ids themselves (no pair lists).
+  const bool sk = M <= kSkinnyMaxM && (long)P <= kMaxDecodePairs && skinny_shape_supported(H, I, true) &&
+                  skinny_shape_supported(I, H, false) &&
+                  (!a.sgu || (skinny_shape_supported(H, SI, true) && skinny_shape_supported(SI, H, false)));
+  // 1. router logits and top-k (skipped with forced routing); decode-size
+  // batches take the small-tile router
   if ((err = mark(0)) != hipSuccess) return err;
   if (!a.ids_in) {
-    hipLaunchKernelGGL(router_kernel,
-                       dim3((M + kRouterTokens - 1) / kRouterTokens, (E + kRouterExperts - 1) / kRouterExperts),
-                       dim3(kGThreads), 0, st, a.x, a.router, M, H, E, a.logits);
+    if (router_small_supported(M, H, E, k))
+      hipLaunchKernelGGL(router_small_kernel, dim3((E + 15) / 16, (M + 15) / 16), dim3(kRsWaves * kWave),
+                         0, st, a.x, a.router, M, H, E, a.logits);
+    else
+      hipLaunchKernelGGL(router_kernel,
+                         dim3((M + kRouterTokens - 1) / kRouterTokens, (E + kRouterExperts - 1) / kRouterExperts),
+                         dim3(kGThreads), 0, st, a.x, a.router, M, H, E, a.logits);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if ((err = launch_topk(a.logits, M, E, k, a.ids, a.tw, nullptr, st)) != hipSuccess) return err;
   }
-  // 2. pair lists per expert
+  // 2. pair lists per expert (not for the skinny GEMMs)
   if ((err = mark(1)) != hipSuccess) return err;
-  hipLaunchKernelGGL(plan_lists_kernel, dim3(E), dim3(256), 0, st, a.ids, P, a.lists, M, a.counts);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (!sk) {
+    hipLaunchKernelGGL(plan_lists_kernel, dim3(E), dim3(256), 0, st, a.ids, P, a.lists, M, a.counts);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   // 3. shared gate/up (and 6. shared down): on the side stream unless
   // stage events are asked for
   if ((err = mark(2)) != hipSuccess) return err;
   const bool side = a.sgu && !a.events && !a.inline_shared;
-  // Few tokens (decode-size batches): every expert GEMM on the skinny
-  // kernels, whose waves each stream their own weight rows.
-  const bool sk = M <= kSkinnyMaxM && skinny_shape_supported(H, I, true) &&
-                  skinny_shape_supported(I, H, false) &&
-                  (!a.sgu || (skinny_shape_supported(H, SI, true) && skinny_shape_supported(SI, H, false)));
   auto sk_launch = [&](const uint16_t *A, int a_rows, const void *w, const uint8_t *ws,
-                       const float *alpha, uint16_t *c, int c_rows, const int32_t *lists,
-                       const int32_t *counts, int E_, int K, int wrows, int ncols, bool gate_up,
-                       int wfmt, hipStream_t s) -> hipError_t {
+                       const float *alpha, uint16_t *c, int c_rows, const int32_t *ids, int E_,
+                       int K, int wrows, int ncols, bool gate_up, int wfmt,
+                       hipStream_t s) -> hipError_t {
     SkinnyArgs g{};
     g.a = A;
     g.a_rows = a_rows;
@@ -968,9 +1038,7 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
     g.alpha = alpha;
     g.c = c;
     g.c_rows = c_rows;
-    g.lists = lists;
-    g.counts = counts;
-    g.list_stride = M;
+    g.ids = ids;
     g.top_k = k;
     g.nrows = M;
     g.K = K;
@@ -1028,8 +1096,8 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
   };
   auto shared_down = [&]() -> hipError_t {
     if (sk)
-      return sk_launch(a.sact, M, a.sdown, a.s_down, a.a_down, a.sh, M, nullptr, nullptr, 1, SI, H,
-                       H, false, a.s_gu ? kNvfp4 : kBf16, sst);
+      return sk_launch(a.sact, M, a.sdown, a.s_down, a.a_down, a.sh, M, nullptr, 1, SI, H, H, false,
+                       a.s_gu ? kNvfp4 : kBf16, sst);
     if (a.s_gu) return nv_shared(kRoutedDown);
     GemmArgs sdn{};
     sdn.a = a.sact;
@@ -1043,8 +1111,8 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
     return launch_gemm<kSharedDown>(sdn, (M + kBM - 1) / kBM, H / kBN, sst);
   };
   if (a.sgu && sk) {
-    if ((err = sk_launch(a.x, M, a.sgu, a.s_gu, a.a_gu, a.sact, M, nullptr, nullptr, 1, H, 2 * SI, SI,
-                         true, a.s_gu ? kNvfp4 : kBf16, sst)) != hipSuccess)
+    if ((err = sk_launch(a.x, M, a.sgu, a.s_gu, a.a_gu, a.sact, M, nullptr, 1, H, 2 * SI, SI, true,
+                         a.s_gu ? kNvfp4 : kBf16, sst)) != hipSuccess)
       return err;
     if (side) {
       if ((err = shared_down()) != hipSuccess) return err;
@@ -1082,14 +1150,14 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
   if (sk) {
     const bool bf = a.bw13 != nullptr;
     if ((err = sk_launch(a.x, M, bf ? (const void *)a.bw13 : (const void *)a.w13, bf ? nullptr : a.s13,
-                         bf ? nullptr : a.a13, a.act, P, a.lists, a.counts, E, H, 2 * I, I, true,
+                         bf ? nullptr : a.a13, a.act, P, a.ids, E, H, 2 * I, I, true,
                          bf ? kBf16 : kNvfp4, st)) != hipSuccess)
       return err;
     // 5. routed down
     if ((err = mark(4)) != hipSuccess) return err;
     if ((err = sk_launch(a.act, P, bf ? (const void *)a.bw2 : (const void *)a.w2, bf ? nullptr : a.s2,
-                         bf ? nullptr : a.a2, a.y, P, a.lists, a.counts, E, I, H, H, false,
-                         bf ? kBf16 : kNvfp4, st)) != hipSuccess)
+                         bf ? nullptr : a.a2, a.y, P, a.ids, E, I, H, H, false, bf ? kBf16 : kNvfp4,
+                         st)) != hipSuccess)
       return err;
   } else if (a.bw13) {
     // BF16 experts: gemm_kernel on the pair lists (the row tiles of every

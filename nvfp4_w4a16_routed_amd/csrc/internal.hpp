@@ -173,10 +173,10 @@ struct SkinnyArgs {
   const uint8_t *ws;      // E4M3 block scales [E][wrows][K / 16] (NVFP4), else NULL
   const float *alpha;     // per-expert global scales [E] (NVFP4), else NULL
   uint16_t *c;            // output rows [c_rows, ldc]
-  const int32_t *lists;   // [E][list_stride] pair indices of each expert (NULL: rows 0 .. nrows - 1)
-  const int32_t *counts;  // [E]
-  int list_stride, top_k;
-  int nrows;              // without lists: the rows (tokens)
+  const int32_t *ids;     // routed: expert ids [nrows * top_k] (pair p = t * top_k + j); NULL:
+                          // one expert whose rows are 0 .. nrows - 1
+  int top_k;
+  int nrows;              // tokens
   int a_rows, c_rows;     // extents of A and C (rows)
   int K, wrows;           // reduction length; weight rows per expert
   int ncols, ldc, I;      // output columns; output row length; gate/up: offset of the up rows
@@ -184,8 +184,9 @@ struct SkinnyArgs {
 };
 
 // gate_up: c[row, n] = bf16(swiglu(alpha a . W[n], alpha a . W[I + n])), n < ncols;
-// else c[row, h] = bf16(alpha a . W[h]).  A row of list entry p: p / top_k
-// (gate/up) or p (down); output row p.  wfmt: kNvfp4 or kBf16.
+// else c[row, h] = bf16(alpha a . W[h]).  Routed: the rows of expert e are
+// its pairs p, with A row p / top_k (gate/up) or p (down) and output row p;
+// nrows * top_k <= 512.  wfmt: kNvfp4 or kBf16.
 hipError_t launch_skinny(const SkinnyArgs &g, bool gate_up, int wfmt, hipStream_t st);
 bool skinny_shape_supported(int K, int ncols, bool gate_up);
 

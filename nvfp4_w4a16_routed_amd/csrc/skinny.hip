@@ -25,7 +25,11 @@
 // order is free: fp32 accumulation), so a lane's weights of a step are 16
 // contiguous bytes (NVFP4) and every weight row is read once per call.
 //
-// The A rows (gathered through the pair lists) are shared by the block's
+// Routed rows: a block finds its group's pairs itself from the routing ids
+// (a histogram of the ids over the experts, then the ranks of its expert's
+// pairs in ascending pair order), so no pair-list pass runs before it.
+//
+// The A rows (the rows of those pairs) are shared by the block's
 // waves: they pass through LDS in chunks of 256 K, two buffers, filled with
 // coalesced 16-byte loads one chunk ahead and swapped at a barrier.  Loading
 // A per wave in the MFMA layout instead (16 rows per instruction, four per
@@ -108,19 +112,39 @@ __global__ void __launch_bounds__(NW * kWave, 4) skinny_kernel(SkinnyArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kSkBuf];
   __shared__ int s_first[kMaxExperts + 1];  // first unit-group of each expert, then the total
   __shared__ int s_wsum[4];
+  __shared__ int s_cnt[kMaxExperts];        // routed: pairs of each expert
+  __shared__ int s_bsum[NW];
+  __shared__ int s_rows[16];                // routed: pair of each row of the group, or -1
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int m = lane & 15, grp = lane >> 4;
   const int C = g.K / kSkCK;  // chunks
   const int KS = 2 * C;       // steps
-  const int nE = g.lists ? g.E : 1;
+  const bool routed = g.ids != nullptr;
+  const int nE = routed ? g.E : 1;
   const int tiles = (g.ncols / CW + NW - 1) / NW;  // column-tile units per group
 
+  // routed: the pairs of each expert, from the routing ids (one pair per
+  // thread: nrows * top_k <= NT); an out-of-range id belongs to no expert
+  int my_id = -1;
+  if (routed) {
+    for (int e = tid; e < nE; e += NT) s_cnt[e] = 0;
+    if (tid < 16) s_rows[tid] = -1;
+    __syncthreads();
+    if (tid < g.nrows * g.top_k) {
+      const int v = g.ids[tid];
+      if ((unsigned)v < (unsigned)nE) {
+        my_id = v;
+        atomicAdd(&s_cnt[v], 1);
+      }
+    }
+    __syncthreads();
+  }
   // groups of 16 rows of each expert, prefix over the experts
   {
     int ng = 0;
-    if (tid < nE) ng = ((g.lists ? g.counts[tid] : g.nrows) + 15) >> 4;
+    if (tid < nE) ng = ((routed ? s_cnt[tid] : g.nrows) + 15) >> 4;
     int incl = ng;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -162,7 +186,19 @@ __global__ void __launch_bounds__(NW * kWave, 4) skinny_kernel(SkinnyArgs g) {
     }
     const int e = lo;
     const int nb = 16 * (gidx - s_first[e]);  // first row of the group
-    const int np = g.lists ? g.counts[e] : g.nrows;
+    const int np = routed ? s_cnt[e] : g.nrows;
+    // routed: rows nb .. nb + 15 of expert e are its pairs of those ranks in
+    // ascending pair order (rank: matching pairs of smaller index)
+    if (routed) {
+      const bool match = my_id == e;
+      const unsigned long long bal = __ballot(match);
+      if (lane == 0) s_bsum[wv] = __popcll(bal);
+      __syncthreads();
+      int rank = __popcll(bal & ((1ull << lane) - 1ull));
+      for (int w = 0; w < wv; ++w) rank += s_bsum[w];
+      if (match && rank >= nb && rank < nb + 16) s_rows[rank - nb] = tid;
+      __syncthreads();
+    }
 
     // waves past the last column tile stream the last tile again (uniform
     // work for the barriers) and store nothing
@@ -176,7 +212,6 @@ __global__ void __launch_bounds__(NW * kWave, 4) skinny_kernel(SkinnyArgs g) {
     const uint32_t wbase = (uint32_t)(wrow * (NV ? g.K / 2 : g.K * 2));
     const uint32_t sbase = (uint32_t)(wrow * (g.K / 16));
     const float alpha = g.alpha ? g.alpha[e] : 1.0f;
-    const int32_t *list = g.lists ? g.lists + (size_t)e * g.list_stride : nullptr;
 
     auto load_w = [&](SkW<WFMT> &w, int ks) {
       const bool ok = ks < KS;
@@ -254,8 +289,8 @@ __global__ void __launch_bounds__(NW * kWave, 4) skinny_kernel(SkinnyArgs g) {
       abase[i] = kOOB;
       const int n = nb + srow;
       if (n < np) {
-        const int p = list ? list[n] : n;
-        abase[i] = (uint32_t)(list && GATE_UP ? p / g.top_k : p) * g.K * 2 + spiece * 16;
+        const int p = routed ? s_rows[srow] : n;
+        abase[i] = (uint32_t)(routed && GATE_UP ? p / g.top_k : p) * g.K * 2 + spiece * 16;
       }
     }
     load_a(0);
@@ -334,7 +369,7 @@ __global__ void __launch_bounds__(NW * kWave, 4) skinny_kernel(SkinnyArgs g) {
     // epilogue: lane holds weight rows 4 grp .. + 3 of row m of the group
     const int n = nb + m;
     if (store && n < np) {
-      const int crow = list ? list[n] : n;
+      const int crow = routed ? s_rows[m] : n;
       if constexpr (GATE_UP) {
         // rows 4 grp + (0, 1, 2, 3) = gate / up of column c0 + 2 grp, then of c0 + 2 grp + 1
         const float g0 = acc[0] * alpha, u0 = acc[1] * alpha;
@@ -369,15 +404,15 @@ bool skinny_shape_supported(int K, int ncols, bool gate_up) {
 
 hipError_t launch_skinny(const SkinnyArgs &g, bool gate_up, int wfmt, hipStream_t st) {
   if (!skinny_shape_supported(g.K, g.ncols, gate_up)) return hipErrorInvalidValue;
-  if (g.lists && (g.E < 1 || g.E > kMaxExperts)) return hipErrorInvalidValue;
+  if (g.ids && (g.E < 1 || g.E > kMaxExperts || (long)g.nrows * g.top_k > SK_NW * kWave))
+    return hipErrorInvalidValue;
   const int cw = gate_up ? 8 : 16;
   const long long tiles = (g.ncols / cw + SK_NW - 1) / SK_NW;
-  // groups of 16 rows: without lists ceil(nrows / 16); with lists at most
-  // one per expert with rows plus one per 16 list entries (the lists hold
-  // nrows * top_k entries in all)
-  const long long pairs = (long long)g.nrows * (g.lists ? g.top_k : 1);
+  // groups of 16 rows: without routing ceil(nrows / 16); routed at most one
+  // per expert with pairs plus one per 16 pairs (nrows * top_k in all)
+  const long long pairs = (long long)g.nrows * (g.ids ? g.top_k : 1);
   const long long groups =
-      g.lists ? (pairs + 15) / 16 + (pairs < g.E ? pairs : g.E) : ((long long)g.nrows + 15) / 16;
+      g.ids ? (pairs + 15) / 16 + (pairs < g.E ? pairs : g.E) : ((long long)g.nrows + 15) / 16;
   const long long units = groups * tiles;
   const bool u4 = SK_U == 4 && (g.K / kSkCK) % 4 == 0;
   if (gate_up) {
