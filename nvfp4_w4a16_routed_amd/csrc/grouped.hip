@@ -1025,11 +1025,11 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
   // 3. shared gate/up (and 6. shared down): on the side stream unless
   // stage events are asked for
   if ((err = mark(2)) != hipSuccess) return err;
-  const bool side = a.sgu && !a.events && !a.inline_shared;
-  auto sk_launch = [&](const uint16_t *A, int a_rows, const void *w, const uint8_t *ws,
-                       const float *alpha, uint16_t *c, int c_rows, const int32_t *ids, int E_,
-                       int K, int wrows, int ncols, bool gate_up, int wfmt,
-                       hipStream_t s) -> hipError_t {
+  // (the skinny GEMMs compute the shared expert in the routed launches)
+  const bool side = a.sgu && !a.events && !a.inline_shared && !sk;
+  auto sk_args = [&](const uint16_t *A, int a_rows, const void *w, const uint8_t *ws,
+                     const float *alpha, uint16_t *c, int c_rows, const int32_t *ids, int E_, int K,
+                     int wrows, int ncols) -> SkinnyArgs {
     SkinnyArgs g{};
     g.a = A;
     g.a_rows = a_rows;
@@ -1047,7 +1047,7 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
     g.ldc = ncols;
     g.I = ncols;
     g.E = E_;
-    return launch_skinny(g, gate_up, wfmt, s);
+    return g;
   };
   hipStream_t sst = st;
   std::unique_lock<std::mutex> side_lock;
@@ -1095,9 +1095,6 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
     return launch_routed<kRoutedDown>(g, (M + kRBM - 1) / kRBM + 1, sst);
   };
   auto shared_down = [&]() -> hipError_t {
-    if (sk)
-      return sk_launch(a.sact, M, a.sdown, a.s_down, a.a_down, a.sh, M, nullptr, 1, SI, H, H, false,
-                       a.s_gu ? kNvfp4 : kBf16, sst);
     if (a.s_gu) return nv_shared(kRoutedDown);
     GemmArgs sdn{};
     sdn.a = a.sact;
@@ -1111,13 +1108,7 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
     return launch_gemm<kSharedDown>(sdn, (M + kBM - 1) / kBM, H / kBN, sst);
   };
   if (a.sgu && sk) {
-    if ((err = sk_launch(a.x, M, a.sgu, a.s_gu, a.a_gu, a.sact, M, nullptr, 1, H, 2 * SI, SI, true,
-                         a.s_gu ? kNvfp4 : kBf16, sst)) != hipSuccess)
-      return err;
-    if (side) {
-      if ((err = shared_down()) != hipSuccess) return err;
-      if ((err = hipEventRecord(sd->join, sst)) != hipSuccess) return err;
-    }
+    // with the routed gate/up below
   } else if (a.sgu && a.s_gu) {
     hipLaunchKernelGGL(iota_list_kernel, dim3((M + 255) / 256), dim3(256), 0, sst, a.sh_lists, M, a.sh_counts);
     if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -1148,17 +1139,22 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
   if ((err = mark(3)) != hipSuccess) return err;
   const int max_row_tiles = (P + kRBM - 1) / kRBM + E;
   if (sk) {
+    // gate/up of the routed experts and of the shared expert in one launch,
+    // then their down projections in another (the shared units read sact,
+    // which the first launch completed)
     const bool bf = a.bw13 != nullptr;
-    if ((err = sk_launch(a.x, M, bf ? (const void *)a.bw13 : (const void *)a.w13, bf ? nullptr : a.s13,
-                         bf ? nullptr : a.a13, a.act, P, a.ids, E, H, 2 * I, I, true,
-                         bf ? kBf16 : kNvfp4, st)) != hipSuccess)
-      return err;
+    const int rf = bf ? kBf16 : kNvfp4, sf = a.s_gu ? kNvfp4 : kBf16;
+    const SkinnyArgs rgu = sk_args(a.x, M, bf ? (const void *)a.bw13 : (const void *)a.w13,
+                                   bf ? nullptr : a.s13, bf ? nullptr : a.a13, a.act, P, a.ids, E, H,
+                                   2 * I, I);
+    const SkinnyArgs sgu = sk_args(a.x, M, a.sgu, a.s_gu, a.a_gu, a.sact, M, nullptr, 1, H, 2 * SI, SI);
+    if ((err = launch_skinny(rgu, rf, a.sgu ? &sgu : nullptr, sf, true, st)) != hipSuccess) return err;
     // 5. routed down
     if ((err = mark(4)) != hipSuccess) return err;
-    if ((err = sk_launch(a.act, P, bf ? (const void *)a.bw2 : (const void *)a.w2, bf ? nullptr : a.s2,
-                         bf ? nullptr : a.a2, a.y, P, a.ids, E, I, H, H, false, bf ? kBf16 : kNvfp4,
-                         st)) != hipSuccess)
-      return err;
+    const SkinnyArgs rdn = sk_args(a.act, P, bf ? (const void *)a.bw2 : (const void *)a.w2,
+                                   bf ? nullptr : a.s2, bf ? nullptr : a.a2, a.y, P, a.ids, E, I, H, H);
+    const SkinnyArgs sdn = sk_args(a.sact, M, a.sdown, a.s_down, a.a_down, a.sh, M, nullptr, 1, SI, H, H);
+    if ((err = launch_skinny(rdn, rf, a.sgu ? &sdn : nullptr, sf, false, st)) != hipSuccess) return err;
   } else if (a.bw13) {
     // BF16 experts: gemm_kernel on the pair lists (the row tiles of every
     // expert, in expert order; blocks past the last tile exit at once)
@@ -1234,7 +1230,7 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
   if ((err = mark(5)) != hipSuccess) return err;
   if (side) {
     if ((err = hipStreamWaitEvent(st, sd->join, 0)) != hipSuccess) return err;
-  } else if (a.sgu) {
+  } else if (a.sgu && !sk) {
     if ((err = shared_down()) != hipSuccess) return err;
   }
   // 7. combine + shared add (a precomputed shared output: once its event

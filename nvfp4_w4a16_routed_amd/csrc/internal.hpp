@@ -186,8 +186,11 @@ struct SkinnyArgs {
 // gate_up: c[row, n] = bf16(swiglu(alpha a . W[n], alpha a . W[I + n])), n < ncols;
 // else c[row, h] = bf16(alpha a . W[h]).  Routed: the rows of expert e are
 // its pairs p, with A row p / top_k (gate/up) or p (down) and output row p;
-// nrows * top_k <= 512.  wfmt: kNvfp4 or kBf16.
-hipError_t launch_skinny(const SkinnyArgs &g, bool gate_up, int wfmt, hipStream_t st);
+// nrows * top_k <= 512.  One launch computes the routed GEMM r (weights in
+// format wfmt_r: kNvfp4 or kBf16) and, if sh is non-NULL, the dense GEMM sh
+// (the shared expert: ids NULL, format wfmt_s) with it.
+hipError_t launch_skinny(const SkinnyArgs &r, int wfmt_r, const SkinnyArgs *sh, int wfmt_s, bool gate_up,
+                         hipStream_t st);
 bool skinny_shape_supported(int K, int ncols, bool gate_up);
 
 // The MoE block with grouped MFMA GEMMs (any M >= 1).

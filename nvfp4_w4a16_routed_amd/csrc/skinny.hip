@@ -15,8 +15,8 @@
 // owns 16 weight rows (gate/up: 8 output columns, their gate and up rows
 // interleaved; down: 16 output rows) and walks K in steps of 128 with the
 // next steps' weights in flight in registers, multiplying each step on
-// v_mfma_f32_16x16x32_bf16 against one group of 16 A rows (blockIdx.z: the
-// group; an expert with more rows has one block per group and column tile):
+// v_mfma_f32_16x16x32_bf16 against one group of 16 A rows (an expert with
+// more rows has one block per group and column tile):
 //   A operand (16 x 32): lane l holds weight row l % 16, K slots 8 (l / 16)..
 //   B operand (32 x 16): lane l holds A row l % 16 of the group, same K slots
 //   D (16 x 16): lane l holds weight rows 4 (l / 16) .. + 3 of A row l % 16.
@@ -53,12 +53,7 @@ namespace flint {
 
 namespace {
 
-#ifndef SK_NW
-#define SK_NW 8
-#endif
-#ifndef SK_U
-#define SK_U 2
-#endif
+constexpr int kSkWaves = 8;      // waves per block
 constexpr int kSkK = 128;        // K per step
 constexpr int kSkCK = 256;       // K per A chunk (two steps)
 constexpr int kSkRowB = kSkCK * 2 + 16;  // bytes of one A row in LDS (16 pad: rows 4 banks apart)
@@ -100,21 +95,32 @@ struct SkW<kBf16> {
 // the blocks past the last unit (the grid is a bound on the units) exit at
 // once.  (A shared work counter instead costs every block an atomic round
 // trip before its first weight load.)
+// LDS of a block.
+struct SkLds {
+  __attribute__((aligned(16))) uint8_t a[2 * kSkBuf];  // A chunk buffers
+  int first[kMaxExperts + 1];  // first unit-group of each expert, then the total
+  int wsum[4];
+  int cnt[kMaxExperts];        // routed: pairs of each expert
+  int bsum[16];
+  int rows[16];                // routed: pair of each row of the group, or -1
+};
+
+// Unit `unit` of the GEMM g (the whole block takes part).
 template <bool GATE_UP, int WFMT, int NW, int U>
-__global__ void __launch_bounds__(NW * kWave, 4) skinny_kernel(SkinnyArgs g) {
+__device__ __forceinline__ void sk_unit(const SkinnyArgs &g, const int unit, SkLds &L) {
   constexpr int CW = GATE_UP ? 8 : 16;  // output columns per wave
   constexpr bool NV = WFMT == kNvfp4;
   constexpr int NT = NW * kWave;
   constexpr int WD = NV ? 2 * U : 2;
   constexpr int SPT = 16 * (kSkCK / 8) / NT;  // A pieces (16 bytes) per thread per chunk
-  static_assert(SPT * NT == 16 * (kSkCK / 8) && U % 2 == 0, "block shape");
+  static_assert(SPT * NT == 16 * (kSkCK / 8) && U % 2 == 0 && NW <= 16, "block shape");
   static_assert(kMaxExperts <= 4 * kWave && NT >= kMaxExperts, "one thread per expert in the prefix");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kSkBuf];
-  __shared__ int s_first[kMaxExperts + 1];  // first unit-group of each expert, then the total
-  __shared__ int s_wsum[4];
-  __shared__ int s_cnt[kMaxExperts];        // routed: pairs of each expert
-  __shared__ int s_bsum[NW];
-  __shared__ int s_rows[16];                // routed: pair of each row of the group, or -1
+  uint8_t *const lds = L.a;
+  int *const s_first = L.first;
+  int *const s_wsum = L.wsum;
+  int *const s_cnt = L.cnt;
+  int *const s_bsum = L.bsum;
+  int *const s_rows = L.rows;
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -172,7 +178,6 @@ __global__ void __launch_bounds__(NW * kWave, 4) skinny_kernel(SkinnyArgs g) {
 
   __syncthreads();  // publishes s_first
   {
-    const int unit = blockIdx.x;
     const int total = s_first[nE] * tiles;
     if (unit >= total) return;  // the whole block
     const int gidx = unit / tiles, tile = unit - gidx * tiles;
@@ -387,13 +392,37 @@ __global__ void __launch_bounds__(NW * kWave, 4) skinny_kernel(SkinnyArgs g) {
   }
 }
 
-template <bool GU, int WFMT, int U>
-hipError_t sk_launch(const SkinnyArgs &g, long long units, hipStream_t st) {
+// Blocks [0, sh_units) compute the units of sh (the shared expert: every
+// token, first in dispatch order since its units stream more bytes), the
+// others those of r (the routed experts).
+template <bool GATE_UP, int WR, int WS, int NW, int U>
+__global__ void __launch_bounds__(NW * kWave, 4) skinny_kernel(SkinnyArgs r, SkinnyArgs sh, int sh_units) {
+  __shared__ SkLds L;
+  if ((int)blockIdx.x < sh_units)
+    sk_unit<GATE_UP, WS, NW, U>(sh, blockIdx.x, L);
+  else
+    sk_unit<GATE_UP, WR, NW, U>(r, blockIdx.x - sh_units, L);
+}
+
+template <bool GU, int WR, int WS>
+hipError_t sk_launch(const SkinnyArgs &r, const SkinnyArgs &sh, long long sh_units, long long units,
+                     hipStream_t st) {
   if (units <= 0) return hipSuccess;
   if (units > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((skinny_kernel<GU, WFMT, SK_NW, U>), dim3((unsigned)units), dim3(SK_NW * kWave),
-                     0, st, g);
+  hipLaunchKernelGGL((skinny_kernel<GU, WR, WS, kSkWaves, 2>), dim3((unsigned)units), dim3(kSkWaves * kWave),
+                     0, st, r, sh, (int)sh_units);
   return hipGetLastError();
+}
+
+// Units of g: without routing ceil(nrows / 16) groups (exact); routed at
+// most one group per expert with pairs plus one per 16 pairs (a bound).
+long long sk_units(const SkinnyArgs &g, bool gate_up) {
+  const int cw = gate_up ? 8 : 16;
+  const long long tiles = (g.ncols / cw + kSkWaves - 1) / kSkWaves;
+  const long long pairs = (long long)g.nrows * (g.ids ? g.top_k : 1);
+  const long long groups =
+      g.ids ? (pairs + 15) / 16 + (pairs < g.E ? pairs : g.E) : ((long long)g.nrows + 15) / 16;
+  return groups * tiles;
 }
 
 }  // namespace
@@ -402,27 +431,27 @@ bool skinny_shape_supported(int K, int ncols, bool gate_up) {
   return K > 0 && K % kSkCK == 0 && ncols > 0 && ncols % (gate_up ? 8 : 16) == 0;
 }
 
-hipError_t launch_skinny(const SkinnyArgs &g, bool gate_up, int wfmt, hipStream_t st) {
-  if (!skinny_shape_supported(g.K, g.ncols, gate_up)) return hipErrorInvalidValue;
-  if (g.ids && (g.E < 1 || g.E > kMaxExperts || (long)g.nrows * g.top_k > SK_NW * kWave))
-    return hipErrorInvalidValue;
-  const int cw = gate_up ? 8 : 16;
-  const long long tiles = (g.ncols / cw + SK_NW - 1) / SK_NW;
-  // groups of 16 rows: without routing ceil(nrows / 16); routed at most one
-  // per expert with pairs plus one per 16 pairs (nrows * top_k in all)
-  const long long pairs = (long long)g.nrows * (g.ids ? g.top_k : 1);
-  const long long groups =
-      g.ids ? (pairs + 15) / 16 + (pairs < g.E ? pairs : g.E) : ((long long)g.nrows + 15) / 16;
-  const long long units = groups * tiles;
-  const bool u4 = SK_U == 4 && (g.K / kSkCK) % 4 == 0;
+hipError_t launch_skinny(const SkinnyArgs &r, int wfmt_r, const SkinnyArgs *sh, int wfmt_s, bool gate_up,
+                         hipStream_t st) {
+  auto ok = [&](const SkinnyArgs &g) {
+    return skinny_shape_supported(g.K, g.ncols, gate_up) &&
+           (!g.ids || (g.E >= 1 && g.E <= kMaxExperts && (long)g.nrows * g.top_k <= kSkWaves * kWave));
+  };
+  if (!ok(r) || (sh && (!ok(*sh) || sh->ids))) return hipErrorInvalidValue;
+  const long long su = sh ? sk_units(*sh, gate_up) : 0;
+  const long long units = su + sk_units(r, gate_up);
+  const SkinnyArgs &s = sh ? *sh : r;
+  const bool nr = wfmt_r == kNvfp4, ns = sh ? wfmt_s == kNvfp4 : nr;
   if (gate_up) {
-    if (wfmt == kNvfp4)
-      return u4 ? sk_launch<true, kNvfp4, 4>(g, units, st) : sk_launch<true, kNvfp4, 2>(g, units, st);
-    return sk_launch<true, kBf16, 2>(g, units, st);
+    if (nr) return ns ? sk_launch<true, kNvfp4, kNvfp4>(r, s, su, units, st)
+                      : sk_launch<true, kNvfp4, kBf16>(r, s, su, units, st);
+    return ns ? sk_launch<true, kBf16, kNvfp4>(r, s, su, units, st)
+              : sk_launch<true, kBf16, kBf16>(r, s, su, units, st);
   }
-  if (wfmt == kNvfp4)
-    return u4 ? sk_launch<false, kNvfp4, 4>(g, units, st) : sk_launch<false, kNvfp4, 2>(g, units, st);
-  return sk_launch<false, kBf16, 2>(g, units, st);
+  if (nr) return ns ? sk_launch<false, kNvfp4, kNvfp4>(r, s, su, units, st)
+                    : sk_launch<false, kNvfp4, kBf16>(r, s, su, units, st);
+  return ns ? sk_launch<false, kBf16, kNvfp4>(r, s, su, units, st)
+            : sk_launch<false, kBf16, kBf16>(r, s, su, units, st);
 }
 
 }  // namespace flint
