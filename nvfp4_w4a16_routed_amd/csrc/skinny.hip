@@ -37,9 +37,9 @@
 //
 // E4M3 scales: a lane's two scale bytes of a step sit 8 bytes after those of
 // the previous step, and two-byte loads per step cost the L1 as much as the
-// codes.  Instead every lane loads 8 bytes per four steps (lane group g:
-// its row's 8 scale bytes of step g of the four) and the lanes trade them
-// with ds_bpermute (no LDS storage).
+// codes.  Instead every lane loads 16 bytes per eight steps (lane group g:
+// its row's scale bytes of steps 2 g and 2 g + 1 of the eight) and the lanes
+// trade them with ds_bpermute (no LDS storage).
 //
 // NVFP4 codes are converted exactly: E2M1 pair to fp32 (hardware
 // converter), times the block's E4M3 scale (the product has at most 6
@@ -54,6 +54,7 @@ namespace flint {
 namespace {
 
 constexpr int kSkWaves = 8;      // waves per block
+constexpr int kSkXcds = 8;       // XCDs the blocks of a launch are dealt to in turn
 constexpr int kSkK = 128;        // K per step
 constexpr int kSkCK = 256;       // K per A chunk (two steps)
 constexpr int kSkRowB = kSkCK * 2 + 16;  // bytes of one A row in LDS (16 pad: rows 4 banks apart)
@@ -85,7 +86,7 @@ struct SkW<kBf16> {
 
 // GATE_UP: output column n from weight rows n (gate) and I + n (up), 8 per
 // wave; else output column h from weight row h, 16 per wave.
-// NW waves per block; U chunks per loop pass (the weight ring: NVFP4 2 U
+// NW waves per block; U = 4 chunks per loop pass (the weight ring: NVFP4 4
 // steps in flight, 16 bytes per lane each; bf16 2 steps, 64 bytes).
 //
 // Block b computes unit b: a unit is (expert, group of 16 of its rows, NW
@@ -111,9 +112,9 @@ __device__ __forceinline__ void sk_unit(const SkinnyArgs &g, const int unit, SkL
   constexpr int CW = GATE_UP ? 8 : 16;  // output columns per wave
   constexpr bool NV = WFMT == kNvfp4;
   constexpr int NT = NW * kWave;
-  constexpr int WD = NV ? 2 * U : 2;
+  constexpr int WD = NV ? 4 : 2;
   constexpr int SPT = 16 * (kSkCK / 8) / NT;  // A pieces (16 bytes) per thread per chunk
-  static_assert(SPT * NT == 16 * (kSkCK / 8) && U % 2 == 0 && NW <= 16, "block shape");
+  static_assert(SPT * NT == 16 * (kSkCK / 8) && U == 4 && NW <= 16, "block shape");
   static_assert(kMaxExperts <= 4 * kWave && NT >= kMaxExperts, "one thread per expert in the prefix");
   uint8_t *const lds = L.a;
   int *const s_first = L.first;
@@ -178,9 +179,22 @@ __device__ __forceinline__ void sk_unit(const SkinnyArgs &g, const int unit, SkL
 
   __syncthreads();  // publishes s_first
   {
-    const int total = s_first[nE] * tiles;
-    if (unit >= total) return;  // the whole block
-    const int gidx = unit / tiles, tile = unit - gidx * tiles;
+    int gidx, tile;
+    if (routed) {
+      if (unit >= s_first[nE] * tiles) return;  // the whole block
+      gidx = unit / tiles;
+      tile = unit - gidx * tiles;
+    } else {
+      // Dense (every row, one expert): the groups of a column tile read the
+      // same weights, so they take block ids kSkXcds apart (blocks are
+      // dealt to the XCDs in turn): the same XCD, hence its L2, at about
+      // the same time.  Tiles are padded to a multiple of kSkXcds.
+      const int ng = s_first[1];
+      const int slot = unit % kSkXcds, round = unit / kSkXcds;
+      gidx = round % ng;
+      tile = (round / ng) * kSkXcds + slot;
+      if (tile >= tiles) return;  // the whole block
+    }
     // expert of group gidx: the last e with s_first[e] <= gidx (experts
     // without rows share their successor's first group)
     int lo = 0, hi = nE - 1;
@@ -233,26 +247,29 @@ __device__ __forceinline__ void sk_unit(const SkinnyArgs &g, const int unit, SkL
                            kPolicyStream));
       }
     };
-    // scale bytes of steps ks .. ks + 3: lane group grp loads its row's 8
-    // bytes of step ks + grp (the two bytes of each lane group of that step)
-    v2u32_t sblk = {0u, 0u};
+    // scale bytes of steps ks .. ks + 7: lane group grp loads its row's 16
+    // bytes of steps ks + 2 grp, ks + 2 grp + 1 (each step's 8 bytes: two
+    // per lane group of that step)
+    u32x4_t sblk = {0u, 0u, 0u, 0u};
     auto load_s = [&](int ks) {
       if constexpr (NV)
         sblk = __builtin_bit_cast(
-            v2u32_t, __builtin_amdgcn_raw_buffer_load_b64(
-                         rs, ks + grp < KS ? sbase + (ks + grp) * (kSkK / 16) : kOOB, 0,
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                         rs, ks + 2 * grp < KS ? sbase + (ks + 2 * grp) * (kSkK / 16) : kOOB, 0,
                          kPolicyStream));
     };
-    // -> sc[i]: this lane's two scale bytes of step ks + i (low half)
+    // -> sc[j]: this lane's two scale bytes (low half) of step i0 + j of the
+    // eight whose bytes sblk holds
     uint32_t sc[4];
-    auto take_s = [&]() {
+    auto take_s = [&](const int i0) {
       if constexpr (NV) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int src = (i * 16 + m) * 4;
-          const uint32_t d0 = __builtin_amdgcn_ds_bpermute(src, (int)sblk.x);
-          const uint32_t d1 = __builtin_amdgcn_ds_bpermute(src, (int)sblk.y);
-          sc[i] = ((grp >> 1) ? d1 : d0) >> half_sh;
+        for (int j = 0; j < 4; ++j) {
+          const int i = i0 + j;
+          const int src = ((i >> 1) * 16 + m) * 4;
+          const uint32_t d0 = __builtin_amdgcn_ds_bpermute(src, (int)sblk[(i & 1) * 2]);
+          const uint32_t d1 = __builtin_amdgcn_ds_bpermute(src, (int)sblk[(i & 1) * 2 + 1]);
+          sc[j] = ((grp >> 1) ? d1 : d0) >> half_sh;
         }
       }
     };
@@ -276,13 +293,13 @@ __device__ __forceinline__ void sk_unit(const SkinnyArgs &g, const int unit, SkL
 
     SkW<WFMT> wq[WD];
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    // The first scales and weight steps go out before the pair-list reads
-    // that the A rows wait for; then chunk 0 into buffer 0, chunk 1 on its
-    // way and the last weight steps of the ring.  The issue order after the
-    // scales and after chunk 1 is the loop's (a chunk pair's scales, then
-    // per chunk its A load and its two steps' weight loads), so the loop's
-    // waits are the same from its first pass on (sched_barrier: the
-    // scheduler keeps this order).
+    // The first scales and weight steps go out before the row lookups that
+    // the A rows wait for; then chunk 0 into buffer 0, chunk 1 on its way
+    // and the last weight steps of the ring.  After the scales and after
+    // chunk 1 at least as many loads follow as in the loop (per chunk its
+    // A load and its two steps' weight loads, the scales of eight steps in
+    // every fourth chunk), so the loop's waits are the same from its first
+    // pass on (sched_barrier: the scheduler keeps this order).
     load_s(0);
 #pragma unroll
     for (int d = 0; d < WD - 2; ++d) load_w(wq[d], d);
@@ -338,13 +355,16 @@ __device__ __forceinline__ void sk_unit(const SkinnyArgs &g, const int unit, SkL
     // buffer and chunk c + 2 is requested before the two steps of chunk c,
     // so a wait for the A loads never waits for the weights of the steps
     // ahead.  Every chunk issues the same loads (past the end: out of
-    // range, zeros), and the loop runs U chunks per pass with fixed ring
-    // slots, which keeps the compiler's waits exact.  P: c % U.
+    // range, zeros), and the loop runs U = 4 chunks per pass with fixed
+    // ring slots, which keeps the compiler's waits exact; the last C % 4
+    // chunks run after it, straight-line.  P: c % 4.  The scales of eight
+    // steps are traded among the lanes four steps at a time (P = 0, 2); the
+    // next eight steps' are requested after the second trade.
     auto chunk = [&](int c, auto par) {
       constexpr int P = decltype(par)::value;
-      if (P % 2 == 0) {
-        // a pair's scales, and the next pair's requested
-        take_s();
+      if (P == 0) take_s(0);
+      if (P == 2) {
+        take_s(4);
         __builtin_amdgcn_sched_barrier(0);
         load_s(2 * c + 4);
       }
@@ -357,19 +377,15 @@ __device__ __forceinline__ void sk_unit(const SkinnyArgs &g, const int unit, SkL
       __syncthreads();
     };
     int c = 0;
-    for (; c + U - 1 < C; c += U) {
+    for (; c + 3 < C; c += 4) {
       chunk(c, std::integral_constant<int, 0>{});
       chunk(c + 1, std::integral_constant<int, 1>{});
-      if constexpr (U == 4) {
-        chunk(c + 2, std::integral_constant<int, 2>{});
-        chunk(c + 3, std::integral_constant<int, 3>{});
-      }
+      chunk(c + 2, std::integral_constant<int, 2>{});
+      chunk(c + 3, std::integral_constant<int, 3>{});
     }
     if (c < C) chunk(c, std::integral_constant<int, 0>{});
     if (c + 1 < C) chunk(c + 1, std::integral_constant<int, 1>{});
-    if constexpr (U == 4) {
-      if (c + 2 < C) chunk(c + 2, std::integral_constant<int, 2>{});
-    }
+    if (c + 2 < C) chunk(c + 2, std::integral_constant<int, 2>{});
 
     // epilogue: lane holds weight rows 4 grp .. + 3 of row m of the group
     const int n = nb + m;
@@ -396,7 +412,7 @@ __device__ __forceinline__ void sk_unit(const SkinnyArgs &g, const int unit, SkL
 // token, first in dispatch order since its units stream more bytes), the
 // others those of r (the routed experts).
 template <bool GATE_UP, int WR, int WS, int NW, int U>
-__global__ void __launch_bounds__(NW * kWave, 4) skinny_kernel(SkinnyArgs r, SkinnyArgs sh, int sh_units) {
+__global__ void __launch_bounds__(NW * kWave, 6) skinny_kernel(SkinnyArgs r, SkinnyArgs sh, int sh_units) {
   __shared__ SkLds L;
   if ((int)blockIdx.x < sh_units)
     sk_unit<GATE_UP, WS, NW, U>(sh, blockIdx.x, L);
@@ -409,7 +425,7 @@ hipError_t sk_launch(const SkinnyArgs &r, const SkinnyArgs &sh, long long sh_uni
                      hipStream_t st) {
   if (units <= 0) return hipSuccess;
   if (units > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((skinny_kernel<GU, WR, WS, kSkWaves, 2>), dim3((unsigned)units), dim3(kSkWaves * kWave),
+  hipLaunchKernelGGL((skinny_kernel<GU, WR, WS, kSkWaves, 4>), dim3((unsigned)units), dim3(kSkWaves * kWave),
                      0, st, r, sh, (int)sh_units);
   return hipGetLastError();
 }
@@ -422,7 +438,7 @@ long long sk_units(const SkinnyArgs &g, bool gate_up) {
   const long long pairs = (long long)g.nrows * (g.ids ? g.top_k : 1);
   const long long groups =
       g.ids ? (pairs + 15) / 16 + (pairs < g.E ? pairs : g.E) : ((long long)g.nrows + 15) / 16;
-  return groups * tiles;
+  return g.ids ? groups * tiles : groups * ((tiles + kSkXcds - 1) / kSkXcds * kSkXcds);
 }
 
 }  // namespace
