@@ -358,22 +358,33 @@ class Workload:
         self.torch.cuda.empty_cache()
 
 
+# The decode entry points run the one-kernel decode path up to this many
+# tokens and the grouped chain on the skinny GEMMs past it.
+DECODE_KERNEL_MAX_M = 16
+
+
 def decode_entry(w: Workload, ms: float, shared: str = "bf16") -> dict:
     cfg = w.cfg
+    skinny_path = cfg["M"] > DECODE_KERNEL_MAX_M
     nb = algorithmic_bytes(cfg, w.U, shared)
     gbps = nb["total"] / (ms * 1e-3) / 1e9
     e = {"workload": cfg["name"], "M": cfg["M"], "E": cfg["E"], "experts": cfg["experts"],
          "touched_experts": w.U, "layers_rotated": w.L, "us_per_call": round(ms * 1e3, 3),
          "tokens_per_s": round(cfg["M"] / (ms * 1e-3), 1),
-         "roofline": {"kernel": "decode_kernel", "bound": "hbm", "achieved": round(gbps, 1),
+         "roofline": {"kernel": "decode_kernel" if skinny_path is False else "skinny chain",
+                      "bound": "hbm", "achieved": round(gbps, 1),
                       "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                       "bytes_per_launch": nb["total"], "avg_launch_us": round(ms * 1e3, 3)}}
-    if cfg["M"] >= 64:
+    if skinny_path:
+        # past 16 tokens the decode entry points run the grouped chain with
+        # the skinny MFMA GEMMs: whole-call bytes over the call's time above,
+        # and the products against the bf16 matrix-core peak here
         fl = flops(cfg)["total"]
         tf = fl / (ms * 1e-3) / 1e12
-        e["alu_roofline"] = {"bound": "alu", "achieved": round(tf, 2), "peak": FP32_VALU_TFLOPS,
-                             "unit": "TFLOP/s", "frac": round(tf / FP32_VALU_TFLOPS, 4),
-                             "flops_per_launch": fl}
+        e["path"] = "router + top-k + skinny gate/up + skinny down + combine"
+        e["mfma_roofline"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 5),
+                              "flops_per_launch": fl}
     return e
 
 
