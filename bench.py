@@ -58,6 +58,9 @@ def _args():
     ap.add_argument("--grouped-steps", type=int, default=30)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain fp32 copy of MIB MiB 5 times (HBM counter scale)")
+    ap.add_argument("--mfma-calibration", type=int, default=0, metavar="N",
+                    help="only time a dense bf16 N x N x N product through torch on random data "
+                         "(the vendor GEMM's rate, and the MFMA counters' scale)")
     return ap.parse_args()
 
 
@@ -110,6 +113,31 @@ def copy_calibration(torch, mib: int):
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration": "torch.neg fp32", "bytes_read_per_launch": n,
                       "bytes_written_per_launch": n, "launches": 5}), flush=True)
+
+
+def mfma_calibration(torch, n: int):
+    """A dense bf16 product C = A B (N x N x N, A and B ~ N(0, 1), seeded)
+    through torch (the vendor GEMM library), 10 untimed and 20 timed
+    launches: the rate a tuned library reaches on this part with random data,
+    and a known FLOP count for reading the MFMA busy counters."""
+    g = torch.Generator(device="cuda").manual_seed(1234)
+    a = torch.randn((n, n), generator=g, device="cuda").to(torch.bfloat16)
+    b = torch.randn((n, n), generator=g, device="cuda").to(torch.bfloat16)
+    c = torch.empty((n, n), dtype=torch.bfloat16, device="cuda")
+    for _ in range(10):
+        torch.matmul(a, b, out=c)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(20):
+        torch.matmul(a, b, out=c)
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / 20
+    flops = 2.0 * n * n * n
+    print(json.dumps({"mfma_calibration": "torch.matmul bf16 random N(0,1)", "n": n, "flops_per_launch": flops,
+                      "avg_launch_us": round(us, 2), "tflops_per_s": round(flops / us / 1e6, 1),
+                      "of_2500_tflops": round(flops / us / 1e6 / 2500.0, 4)}), flush=True)
 
 
 class HipEvents:
@@ -422,6 +450,9 @@ def main():
 
     import torch
 
+    if a.mfma_calibration:
+        mfma_calibration(torch, a.mfma_calibration)
+        return
     if a.copy_calibration:
         copy_calibration(torch, a.copy_calibration)
         return
