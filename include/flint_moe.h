@@ -165,8 +165,8 @@ typedef struct {
 #define FLINT_WAIT_LOGITS 1         /* a token's router logits */
 #define FLINT_WAIT_SHARED_GATE_UP 2 /* the shared expert's gate/up blocks */
 #define FLINT_WAIT_GATE_UP 4        /* a routed expert's gate/up blocks */
-#define FLINT_WAIT_COMBINE_SHARED 8 /* the shared down blocks of a combine item */
-#define FLINT_WAIT_COMBINE_DOWN 16  /* the routed down blocks of a combine item */
+#define FLINT_WAIT_COMBINE_SHARED 8 /* the shared down blocks of a combined row group */
+#define FLINT_WAIT_COMBINE_DOWN 16  /* reserved (no longer set: each block combines its own rows) */
 #define FLINT_WAIT_LDS 32           /* a wave of the same block */
 #define FLINT_WAIT_PROBE 64         /* the test hook (flint_moe_debug.wait_probe) */
 

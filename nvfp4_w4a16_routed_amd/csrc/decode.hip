@@ -60,7 +60,8 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;  // 16
 constexpr int kRouteTokens = 4;           // tokens per routing item (one load round trip)
 constexpr int kXLdsBytes = kDecodeXStage;  // x staged in LDS when M * H * 2 fits
-constexpr int kSliceBytes = 4096;         // per-wave LDS slice (act cache, combine)
+constexpr int kSliceBytes = 4096;         // per-wave LDS slice (results, act cache)
+constexpr int kMaxRowGroups = 16;         // down row groups per block
 constexpr int kCacheLdsBytes = kWaves * kSliceBytes;
 // Cache-policy operand of a direct global->LDS load that reads at device
 // scope (the SC1 bit, as the device-scope loads in common.hpp use).
@@ -74,8 +75,8 @@ enum WaitKind {
   kWaitLogits = 1,          // a token's tagged router logits
   kWaitSharedGateUp = 2,    // the shared gate/up blocks' flags
   kWaitGateUp = 4,          // the gate/up blocks of a routed expert
-  kWaitCombineShared = 8,   // the shared down blocks of a combine item
-  kWaitCombineDown = 16,    // the routed down blocks of a combine item
+  kWaitCombineShared = 8,   // the shared down blocks of a combined row group
+  kWaitCombineDown = 16,    // (reserved: each block combines its own rows)
   kWaitLds = 32,            // a wave of the same block (LDS counter)
   kWaitProbe = 64           // the test hook's wait
 };
@@ -239,6 +240,9 @@ struct Route {
   int plan_ready;        // the plan is built
   int x_staged;          // waves whose part of x is in LDS
   int sg_ready;          // every shared gate/up block is done
+  int slot_ready[kMaxExperts];  // phase C: the slot's gate/up blocks are done
+  int done_rg[kMaxRowGroups];   // phase C: items done per row group of the block
+  int sums_ready;               // phase C: the fp64 sums are zeroed
 };
 
 // Work balance.  Item (s, j) of a phase (slot s, j < N items per slot)
@@ -851,9 +855,13 @@ decode_kernel(Params P) {
   TRACE(P, 0);
 
   if (threadIdx.x == 0) {
-    R.done_sg = R.done_sd = R.topk_done = R.plan_ready = R.x_staged = R.sg_ready = 0;
+    R.done_sg = R.done_sd = R.topk_done = R.plan_ready = R.x_staged = R.sg_ready = R.sums_ready = 0;
   }
-  if (threadIdx.x < kMaxExperts) R.tokmask[threadIdx.x] = 0ull;
+  if (threadIdx.x < kMaxExperts) {
+    R.tokmask[threadIdx.x] = 0ull;
+    R.slot_ready[threadIdx.x] = 0;
+  }
+  if (threadIdx.x < kMaxRowGroups) R.done_rg[threadIdx.x] = 0;
   __syncthreads();  // publishes the counters
   // Test hook: one wave waits for a word that no block ever sets, so the
   // wait gives up and records kWaitProbe (the host asks for it).
@@ -1049,6 +1057,8 @@ decode_kernel(Params P) {
   wait_x();
   const int U = R.n_active;
   const uint16_t *xl = x_all ? xs : nullptr;
+  // phase C: this block's down row groups (RW output rows each): b, b + nb, ...
+  const int n_rg = (int)blockIdx.x < Gm::N_DN ? (Gm::N_DN - 1 - (int)blockIdx.x) / P.nb + 1 : 0;
 
   // ---- phase B: routed gate/up; block share [b0, b1) of equal cost
   //
@@ -1103,219 +1113,183 @@ decode_kernel(Params P) {
       ia = take_item(&R.next_b, b0);
       load(sa, ia);
     }
-    block_done(&R.done_b, &S->gb[blockIdx.x], P.seq);
+    // The block's last wave past its gate/up items raises the block's flag
+    // (once the stores of all its waves are performed) and zeroes phase C's
+    // fp64 sums, which live in the x staging area that no wave reads any more.
+    stores_performed();
+    int last = 0;
+    if (lane == 0) last = atomicAdd(&R.done_b, 1) == kWaves - 1;
+    if (__builtin_amdgcn_readfirstlane(last)) {
+      if (lane == 0) st_dev(&S->gb[blockIdx.x], P.seq);
+      double *sums = reinterpret_cast<double *>(xs);
+      const int nsum = n_rg * P.M * Gm::DN::RW;
+      for (int i = lane; i < nsum; i += kWave) sums[i] = 0.0;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      if (lane == 0) __hip_atomic_store(&R.sums_ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
   }
   TRACE(P, 4);
 
-  // ---- phase C: routed down; block share [c0, c1) of equal cost
-  const int QC = max(1, per_wave(R.cum_dn[U], P.nb));
+  // ---- phase C: routed down by row group, with the combine
+  //
+  // Block b owns the row groups g = b, b + nb, ... (RW output rows each) and
+  // computes every slot's down item of them, so the combine of its rows
+  // needs no other block's routed results.  An item adds tw * y of its pairs
+  // into the row group's fp64 sums in LDS (each product of two bf16 values
+  // has 16 significant bits, and their sums are exact, so the order of the
+  // additions does not change them), and the wave that completes a row
+  // group's last item rounds the sums, adds the shared output and stores the
+  // rows.  A block's items start at the slot of its own first gate/up item
+  // (done when the block is) and go round the slots; each slot's gate/up
+  // blocks are polled once per block, and a slot known done has its
+  // activations copied with the item's weights (one round trip).
   {
-    const int c0 = first_item(R, R.cum_dn, Gm::N_DN, blockIdx.x * QC);
-    const int c1 = first_item(R, R.cum_dn, Gm::N_DN, (blockIdx.x + 1) * QC);
+    constexpr int RW = Gm::DN::RW;
+    const int n_items = n_rg * U;
+    const int g0 = first_item(R, R.cum_gu, Gm::N_GU, blockIdx.x * QB);
+    const int s_start = U > 0 && g0 < U * Gm::N_GU ? g0 / Gm::N_GU : 0;
+    double *sums = reinterpret_cast<double *>(xs);  // [n_rg][M][RW]
+    const int sum_bytes = (n_rg * P.M * RW * 8 + 15) & ~15;
     const __amdgpu_buffer_rsrc_t rs_w = make_rsrc(P.w2, (size_t)P.E * H * DN_RSZ);
     const __amdgpu_buffer_rsrc_t rs_s =
         make_rsrc(FMT == kNvfp4 ? (const void *)P.s2 : (const void *)P.w2,
                   FMT == kNvfp4 ? (size_t)P.E * H * (I / 16) : 0);
     const __amdgpu_buffer_rsrc_t rs_o = make_rsrc(P.y, (size_t)P.M * k * H * 2);
+    // activation rows of an item: the first kCache in the wave's slice, the
+    // next kCacheX in its part of the staging area after the sums, any
+    // further ones read from global memory per use
+    constexpr int kCache = (kSliceBytes - Gm::OUT_BYTES) / (2 * I);
+    static_assert(kCache >= 1, "activation cache");
+    const int per_wave_el = (kXLdsBytes - sum_bytes) / kWaves / 2 / 8 * 8;
+    const int kCacheX = per_wave_el / I;
+    uint16_t *xpart = xs + sum_bytes / 2 + (size_t)wv * per_wave_el;
+    bool sums_seen = false;
     struct St {
       DownW<FMT, I> w;
       float alpha;
+      bool act;  // the activations were requested with the weights
     };
-    auto load = [&](St &st, int i) {
-      const bool ok = i < c1;
-      const int e = __builtin_amdgcn_readfirstlane(ok ? R.active[i / Gm::N_DN] : 0);
-      down_load(st.w, rs_w, ok ? (uint32_t)e * H * DN_RSZ : kOOB, rs_s,
-                ok ? (uint32_t)e * H * (I / 16) : kOOB, ok ? (i % Gm::N_DN) * Gm::DN::RW : 0);
-      st.alpha = FMT == kNvfp4 ? P.a2[e] : 1.0f;
+    auto item_of = [&](int f, int &s, int &h_base, int &lr) {
+      lr = f / U;
+      s = s_start + (f - lr * U);
+      if (s >= U) s -= U;
+      h_base = ((int)blockIdx.x + lr * P.nb) * RW;
     };
-    // The first time a wave meets an expert it waits for the blocks owning
-    // that expert's gate/up items, then copies the activations of the
-    // expert's first pairs into its LDS slice, so the item loop reads them
-    // from LDS and only weight loads are in flight between items.
-    // Rows past the slice go to the wave's part of the x staging area once
-    // every wave of the block is past its gate/up items (the only readers
-    // of x there); any further rows are read from global memory per use.
-    constexpr int kCache = (kSliceBytes - Gm::OUT_BYTES) / (2 * I);  // rows per slice
-    constexpr int kCacheX = kXLdsBytes / kWaves / (2 * I);           // rows in the x area
-    static_assert(kCache >= 1, "activation cache");
-    uint16_t *xpart = xs + (size_t)wv * (kXLdsBytes / kWaves / 2);
-    int cur = -1;
-    auto run = [&](const St &st, int i) {
-      const int s = i / Gm::N_DN;
-      const int h_base = (i % Gm::N_DN) * Gm::DN::RW;
+    auto issue_act = [&](int s) {
       const int *pr = R.pairs + R.offs[s];
       const int np = R.offs[s + 1] - R.offs[s];
       const int nc = np < kCache ? np : kCache;
       const int nx = np - nc < kCacheX ? np - nc : kCacheX;
-      if (s != cur) {
-        cur = s;
-        wave_wait_flags(S->gb, owner_block(R, R.cum_gu, s, 0, QB, P.nb),
-                        owner_block(R, R.cum_gu, s, Gm::N_GU - 1, QB, P.nb) + 1, P.seq, P.polls, S,
-                        kWaitGateUp);
-        TRACE_FIRST(P, 10);
-        if (nx > 0) wait_lds_at_least(&R.done_b, kWaves, S);
-        for (int j = 0; j < nc + nx; ++j)  // every row's copies in flight at once
-          issue_copy_to_lds<true>(j < nc ? slice + (size_t)j * I : xpart + (size_t)(j - nc) * I,
-                                  P.act + (size_t)pr[j] * I, I / 8, 0, 1);
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the rows are in LDS
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        TRACE_FIRST(P, 12);
+      for (int j = 0; j < nc + nx; ++j)
+        issue_copy_to_lds<true>(j < nc ? slice + (size_t)j * I : xpart + (size_t)(j - nc) * I,
+                                P.act + (size_t)pr[j] * I, I / 8, 0, 1);
+    };
+    // The combine of row group lr (rows h_base ..): the rounded sums plus the
+    // shared output, for every token.
+    auto combine = [&](int lr, int h_base) {
+      const double *gs = sums + (size_t)lr * P.M * RW;
+      TRACE(P, 6);
+      if (P.sgu) {
+        // the blocks holding the shared down items of these rows (done long
+        // before the routed ones)
+        bool done = false;
+        const int j0 = h_base / Gm::SDN::RW, j1 = (h_base + RW - 1) / Gm::SDN::RW;
+        for (int it = 0, nap = 1; it < P.polls; ++it) {
+          bool ok = true;
+          for (int j = j0 + lane; j <= j1; j += kWave) ok &= ld_dev(&S->sd[sh0 + j % nbs]) == P.seq;
+          if (__all(ok)) {
+            done = true;
+            break;
+          }
+          for (int z = 0; z < nap; ++z) __builtin_amdgcn_s_sleep(2);
+          nap = nap < 4 ? nap * 2 : 4;
+        }
+        if (!done) wait_failed(S, kWaitCombineShared);
       }
+      for (int l = lane; l < P.M * RW; l += kWave) {
+        const int t = l / RW, r = l % RW;
+        const float routed = round_bf16((float)gs[t * RW + r]);
+        const size_t o = (size_t)t * H + h_base + r;
+        const float sv = P.sgu ? bf16_to_f32(ld_dev(&P.sh[o])) : P.sh_ext ? bf16_to_f32(P.sh_ext[o]) : 0.0f;
+        P.out[o] = (uint16_t)f32_to_bf16(routed + sv);
+      }
+    };
+    auto load = [&](St &st, int f) {
+      const bool ok = f < n_items;
+      int s = 0, h_base = 0, lr = 0;
+      if (ok) item_of(f, s, h_base, lr);
+      const int e = __builtin_amdgcn_readfirstlane(ok ? R.active[s] : 0);
+      down_load(st.w, rs_w, ok ? (uint32_t)e * H * DN_RSZ : kOOB, rs_s,
+                ok ? (uint32_t)e * H * (I / 16) : kOOB, h_base);
+      st.alpha = FMT == kNvfp4 ? P.a2[e] : 1.0f;
+      // the staging area holds the sums and act rows once every wave of the
+      // block is past its gate/up items
+      if (ok && !sums_seen) {
+        wait_lds_at_least(&R.sums_ready, 1, S);
+        sums_seen = true;
+      }
+      st.act = ok && __hip_atomic_load(&R.slot_ready[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
+      if (st.act) issue_act(s);
+    };
+    auto run = [&](const St &st, int f) {
+      int s, h_base, lr;
+      item_of(f, s, h_base, lr);
+      const int *pr = R.pairs + R.offs[s];
+      const int np = R.offs[s + 1] - R.offs[s];
+      const int nc = np < kCache ? np : kCache;
+      const int nx = np - nc < kCacheX ? np - nc : kCacheX;
+      if (!st.act) {
+        if (__hip_atomic_load(&R.slot_ready[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) {
+          wave_wait_flags(S->gb, owner_block(R, R.cum_gu, s, 0, QB, P.nb),
+                          owner_block(R, R.cum_gu, s, Gm::N_GU - 1, QB, P.nb) + 1, P.seq, P.polls, S,
+                          kWaitGateUp);
+          if (lane == 0)
+            __hip_atomic_store(&R.slot_ready[s], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        issue_act(s);
+      }
+      TRACE_FIRST(P, 10);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the rows are in LDS
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       for (int j = 0; j < nc; ++j)
         down_one<FMT, H, I, kSrcLds>(st.w, slice + (size_t)j * I, st.alpha, j, ob);
       for (int j = 0; j < nx; ++j)
         down_one<FMT, H, I, kSrcLds>(st.w, xpart + (size_t)j * I, st.alpha, nc + j, ob);
       for (int j = nc + nx; j < np; ++j)
         down_one<FMT, H, I, kSrcDevice>(st.w, P.act + (size_t)pr[j] * I, st.alpha, j, ob);
-      store_results<Gm::DN::RW>(
-          rs_o, lane < np ? (uint32_t)((pr[lane] * H + h_base) * 2) : kOOB, ob);
+      // y (an output of the call) and the item's share of the sums
+      store_results<RW>(rs_o, lane < np ? (uint32_t)((pr[lane] * H + h_base) * 2) : kOOB, ob);
+      double *gs = sums + (size_t)lr * P.M * RW;
+      for (int l = lane; l < np * RW; l += kWave) {
+        const int j = l / RW, r = l % RW, p = pr[j];
+        atomicAdd(&gs[(p / k) * RW + r], (double)R.tw[p] * (double)bf16_to_f32(ob[j * RW + r]));
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      int c = 0;
+      if (lane == 0) c = atomicAdd(&R.done_rg[lr], 1);
+      if (__builtin_amdgcn_readfirstlane(c) != U - 1) return;
+      // the row group's last item: the combine of its rows for every token
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      combine(lr, h_base);
     };
     St sa;
-    int ia = take_item(&R.next_c, c0);
+    int ia = take_item(&R.next_c, 0);
     load(sa, ia);
     TRACE(P, 5);
-    while (ia < c1) {
+    while (ia < n_items) {
       __builtin_amdgcn_sched_barrier(0);
       run(sa, ia);
-      ia = take_item(&R.next_c, c0);
+      ia = take_item(&R.next_c, 0);
       load(sa, ia);
     }
-    block_done(&R.done_c, &S->db[blockIdx.x], P.seq);
-  }
-  TRACE(P, 6);
-
-  // ---- combine: item cb (CB output rows) on wave cb * stride
-  constexpr int NCB = H / Gm::CB;
-  const int stride = NW / NCB > 0 ? NW / NCB : 1;
-  for (int cb = (NW >= NCB) ? (gw % stride == 0 ? gw / stride : NCB) : gw; cb < NCB;
-       cb += (NW >= NCB) ? NCB : NW) {
-    const int h0 = cb * Gm::CB;
-    // The blocks holding the shared down items of these rows (done long
-    // before the routed ones), then those owning the routed down items of
-    // rows [h0, h0 + CB) of every slot.  Every poll issues all its loads
-    // before comparing any (one round trip): a chunk's items lie in at most
-    // two blocks' shares when a share holds IPB items or more (the blocks
-    // between the two ends are read one by one otherwise).
-    if (P.sgu) {
-      bool done = false;
-      for (int it = 0, nap = 1; it < P.polls; ++it) {
-        bool ok = true;
-        for (int j = h0 / Gm::SDN::RW + lane; j < (h0 + Gm::CB) / Gm::SDN::RW; j += kWave)
-          ok &= ld_dev(&S->sd[sh0 + j % nbs]) == P.seq;
-        if (__all(ok)) {
-          done = true;
-          break;
-        }
-        for (int z = 0; z < nap; ++z) __builtin_amdgcn_s_sleep(2);
-        nap = nap < 4 ? nap * 2 : 4;
+    // no routed pairs at all: the rows are the shared output alone
+    if (U == 0)
+      for (int lr = wv; lr < n_rg; lr += kWaves) {
+        wait_lds_at_least(&R.sums_ready, 1, S);
+        combine(lr, ((int)blockIdx.x + lr * P.nb) * RW);
       }
-      if (!done) wait_failed(S, kWaitCombineShared);
-    }
-    constexpr int IPB = Gm::CB / Gm::DN::RW;  // down items per combine item
-    bool cdone = false;
-    for (int it = 0, nap = 1; it < P.polls; ++it) {
-      bool ok = true;
-      for (int s0 = 0; s0 < U; s0 += kWave) {
-        const int s = s0 + lane < U ? s0 + lane : U - 1;
-        const int j0 = h0 / Gm::DN::RW;
-        const int b_lo = owner_block(R, R.cum_dn, s, j0, QC, P.nb);
-        const int b_hi = owner_block(R, R.cum_dn, s, j0 + IPB - 1, QC, P.nb);
-        const int f0 = ld_dev(&S->db[b_lo]), f1 = ld_dev(&S->db[b_hi]);
-        ok &= f0 == P.seq && f1 == P.seq;
-        for (int b = b_lo + 1; b < b_hi; ++b) ok &= ld_dev(&S->db[b]) == P.seq;
-      }
-      if (__all(ok)) {
-        cdone = true;
-        break;
-      }
-      for (int z = 0; z < nap; ++z) __builtin_amdgcn_s_sleep(2);
-      nap = nap < 4 ? nap * 2 : 4;
-    }
-    if (!cdone) wait_failed(S, kWaitCombineDown);
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    // y of the rows for a group of tokens is gathered into this wave's LDS
-    // slice with direct loads (one round trip per group), then summed.
-    uint16_t *yl = slice;
-    constexpr int SLICE = kSliceBytes / 2;  // bf16 per slice
-    // tokens per group: at most 4 outputs and 4 gathered chunks per lane
-    const int G = min(4 * kWave / Gm::CB, SLICE / (k * Gm::CB));
-    for (int t0 = 0; t0 < P.M; t0 += (G > 0 ? G : 1)) {
-      const int nt = G > 0 ? min(G, P.M - t0) : 1;
-      float shv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (G > 0) {
-        const int n = nt * k * (Gm::CB / 8);  // 16-byte chunks, <= 4 per lane
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = u * kWave + lane;
-          if (i < n) {
-            const int p = t0 * k + i / (Gm::CB / 8), part = i % (Gm::CB / 8);
-            __builtin_amdgcn_global_load_lds(
-                P.y + (size_t)p * H + h0 + part * 8,
-                (__attribute__((address_space(3))) void *)(yl + (size_t)u * kWave * 8), 16, 0,
-                kCachePolicyDevice);
-          }
-        }
-        if (P.sgu) {
-          // every lane loads (an address in range) with the gathers
-          uint16_t sv[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int o = min(u * kWave + lane, nt * Gm::CB - 1);
-            sv[u] = ld_dev(&P.sh[(size_t)(t0 + o / Gm::CB) * H + h0 + o % Gm::CB]);
-          }
-#pragma unroll
-          for (int u = 0; u < 4; ++u) shv[u] = bf16_to_f32(sv[u]);
-        } else if (P.sh_ext) {
-          // a precomputed shared output: an input, complete before the launch
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int o = min(u * kWave + lane, nt * Gm::CB - 1);
-            shv[u] = bf16_to_f32(P.sh_ext[(size_t)(t0 + o / Gm::CB) * H + h0 + o % Gm::CB]);
-          }
-        }
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): y is in LDS
-        // The lane's four outputs advance together over the pairs, so their
-        // LDS reads are in flight at once; a dropped id adds +0.
-        double acc[4] = {0.0, 0.0, 0.0, 0.0};  // exact: every product has 16 significant bits
-#pragma unroll 4
-        for (int j = 0; j < k; ++j) {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int o = min(u * kWave + lane, nt * Gm::CB - 1);
-            const int tl = o / Gm::CB, hh = o % Gm::CB, p = (t0 + tl) * k + j;
-            float tw = R.tw[p];
-            asm volatile("" : "+v"(tw));  // read for every pair: no branch per pair
-            const float w = (unsigned)R.ids[p] < (unsigned)P.E ? tw : 0.0f;
-            acc[u] += (double)w * (double)bf16_to_f32(yl[(tl * k + j) * Gm::CB + hh]);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int o = u * kWave + lane;
-          if (o < nt * Gm::CB) {
-            const int tl = o / Gm::CB, hh = o % Gm::CB, t = t0 + tl;
-            const float routed = round_bf16((float)acc[u]);
-            P.out[(size_t)t * H + h0 + hh] = (uint16_t)f32_to_bf16(routed + shv[u]);
-          }
-        }
-      } else {
-        // more pairs per token than a slice holds: device-scope loads
-        for (int hh = lane; hh < Gm::CB; hh += kWave) {
-          double acc = 0.0;
-          for (int j = 0; j < k; ++j) {
-            const int p = t0 * k + j;
-            if ((unsigned)R.ids[p] < (unsigned)P.E)
-              acc += (double)R.tw[p] * (double)bf16_to_f32(ld_dev(&P.y[(size_t)p * H + h0 + hh]));
-          }
-          const float sv = P.sgu      ? bf16_to_f32(ld_dev(&P.sh[(size_t)t0 * H + h0 + hh]))
-                           : P.sh_ext ? bf16_to_f32(P.sh_ext[(size_t)t0 * H + h0 + hh])
-                                      : 0.0f;
-          P.out[(size_t)t0 * H + h0 + hh] = (uint16_t)f32_to_bf16(round_bf16((float)acc) + sv);
-        }
-      }
-    }
   }
   TRACE(P, 7);
   TRACE_FLUSH(P);
@@ -1382,6 +1356,10 @@ hipError_t launch(Params P, hipStream_t st) {
     if (gi.nb > kMaxDecodeBlocks) gi.nb = kMaxDecodeBlocks;
   }
   P.nb = gi.nb;
+  // the down row groups of a block and their fp64 sums (in the staging area)
+  const int n_rg = (Gm::N_DN + P.nb - 1) / P.nb;
+  if (n_rg > kMaxRowGroups || (size_t)n_rg * P.M * Gm::DN::RW * 8 > kXLdsBytes / 2)
+    return hipErrorInvalidValue;
   const int nTG = (P.M + kRouteTokens - 1) / kRouteTokens;
   P.n_route = P.ids_in ? 0 : P.E * nTG;  // routing items (expert, token group)
   P.n_sgu = P.sgu ? I / Gm::SGU::RP : 0;  // shared gate/up items (row pairs)

@@ -31,7 +31,7 @@ struct DecodeSync {
   int sg[kMaxSharedBlocks];  // shared gate/up block done
   int sd[kMaxSharedBlocks];  // shared down block done
   int gb[kMaxDecodeBlocks];  // the block's routed gate/up items done
-  int db[kMaxDecodeBlocks];  // the block's routed down items done
+  int db[kMaxDecodeBlocks];  // (unused: kept so the workspace layout does not change)
   int wait_err;              // OR of the kinds of waits that gave up (0 = none)
   int probe;                 // never written: the target of the test hook's wait
 };
