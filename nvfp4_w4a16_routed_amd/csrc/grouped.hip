@@ -658,106 +658,133 @@ __global__ void __launch_bounds__(kGThreads, 1) routed_gemm_kernel(GemmArgs g) {
 }
 
 // Router logits of the grouped path: logits[t, c] = bf16(fp32 x[t] . R[c]).
-// A block takes 32 tokens and up to 128 experts (blockIdx.y: which 128) in
-// tiles of 32; its
-// four waves split K into quarters, and the four partial tiles are added in
-// wave order through LDS (a fixed order: the result does not depend on
-// timing).  Both operands go straight from memory into registers, one K
-// chunk of 64 ahead, in the MFMA's own layout (operand lane l: row l % 32,
-// k = 16 sub + 8 (l / 32) + 0..7 for sub-step sub).  The MFMA forms tiles
-// with experts as rows: lane l holds token l % 32.
-constexpr int kRouterTokens = 32;
-// Experts per router block: one 32-expert tile, so a prefill batch fills
-// the chip with (M / 32) x (E / 32) blocks.
-constexpr int kRouterExperts = 32;
+// A block takes 16 tokens and up to 128 experts (blockIdx.y: which 128);
+// wave w owns experts 32 w .. 32 w + 31 as two 16 x 16 tiles on
+// v_mfma_f32_16x16x32_bf16 (tokens are the first operand), over all of K
+// (in an order that starts at a chunk of the block's own).  K goes in chunks of 128: the block's x rows and router rows of a
+// chunk are moved global -> LDS with direct loads (16 lanes read one row's
+// 256 contiguous bytes), three chunks ahead in four buffers, then read in the MFMA's
+// operand layout (lane l: row l % 16, k = 32 s + 8 (l / 16) + 0..7 of
+// sub-step s).  The 16-byte chunk c of row r sits at position
+// 16 r + (c ^ (r % 16)), so the 16 lanes of a read (16 rows, one chunk)
+// hit 16 different bank groups.  (Reading the operands from memory in the
+// MFMA layout, each load touching 32 rows, ran at a quarter of this rate.)
+constexpr int kRouterTokens = 16;
+constexpr int kRouterExperts = 128;
+constexpr int kRouterK = 128;  // K per chunk
+
+__device__ __forceinline__ int rt_pos(int r, int c) { return r * 16 + (c ^ (r & 15)); }
 
 __global__ void __launch_bounds__(kGThreads, 1) router_kernel(const uint16_t *__restrict__ x,
                                                               const uint16_t *__restrict__ R, int M, int K,
                                                               int E, uint16_t *__restrict__ logits) {
-  __shared__ f32x16_t part[3][4][kWave];  // partial tiles of waves 1..3
-  const int lane = lane_id(), wv = wave_id(), h = lane >> 5, r = lane & 31;
-  const int t0 = blockIdx.x * kRouterTokens;
-  const int e0 = blockIdx.y * kRouterExperts;
-  const int nte = min(kRouterExperts / 32, (E - e0 + 31) / 32);
-  const __amdgpu_buffer_rsrc_t rs_x = make_rsrc(x, (size_t)M * K * 2);
-  const __amdgpu_buffer_rsrc_t rs_r = make_rsrc(R, (size_t)E * K * 2);
-  // this wave's K range: chunks of 64 [c0, c1) (K is a multiple of 64)
-  const int NK = K / 64, c0 = wv * NK / 4, c1 = (wv + 1) * NK / 4;
-  const uint32_t k0 = (uint32_t)(c0 * 128);  // in bytes
-  const uint32_t xo = (uint32_t)min(t0 + r, M - 1) * (uint32_t)(K * 2) + k0 + h * 16;
-  const uint32_t ro = (uint32_t)(e0 + r) * (uint32_t)(K * 2) + k0 + h * 16;  // + 32 j rows
-  const int nk = c1 - c0;
-
-  auto run = [&](auto nt_c) {
-    constexpr int NT = decltype(nt_c)::value;  // expert tiles (E <= 32 NT)
-    f32x16_t acc[NT];
+  // four chunk buffers, in separate arrays (a read of one does not wait for
+  // the direct loads still in flight into another)
+  __shared__ u32x4_t xa0[kRouterTokens * 16], xa1[kRouterTokens * 16], xa2[kRouterTokens * 16],
+      xa3[kRouterTokens * 16];
+  __shared__ u32x4_t rb0[kRouterExperts * 16], rb1[kRouterExperts * 16], rb2[kRouterExperts * 16],
+      rb3[kRouterExperts * 16];
+  const int lane = lane_id(), wv = wave_id();
+  const int t0 = blockIdx.x * kRouterTokens, e0 = blockIdx.y * kRouterExperts;
+  const int nc = K / kRouterK;
+  // direct loads: wave w moves x rows (one instruction: 4 rows) when w == 0,
+  // and router rows 32 w .. 32 w + 31 (eight instructions); lane j of an
+  // instruction fills position 64 i + j = rt_pos(r, c')
+  const int c_lane = (lane & 15);  // position within the row
+  auto src_chunk = [&](int r) { return c_lane ^ (r & 15); };
+  const uint16_t *xrow[4];
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * i + (lane >> 4);
+    xrow[i] = x + (size_t)min(t0 + r, M - 1) * K + src_chunk(r) * 8;
+  }
+  const uint16_t *rrow[8];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[j][i] = 0.0f;
-    u32x4_t a[2][4], b[2][NT][4];
-    // chunk kc's operands; past the wave's range the loads read zeros (an
-    // offset beyond every descriptor), so the MFMAs on them add nothing
-    auto load = [&](auto buf_c, int kc) {
-      constexpr int B = decltype(buf_c)::value;
-      const uint32_t so = kc < nk ? (uint32_t)(kc * 128) : kOOB;
+  for (int i = 0; i < 8; ++i) {
+    const int r = 32 * wv + 4 * i + (lane >> 4);
+    rrow[i] = R + (size_t)min(e0 + r, E - 1) * K + src_chunk(r) * 8;
+  }
+  // Each block starts at its own chunk of K and goes round: blocks that run
+  // at the same time read different router rows' parts, not the same L2
+  // lines at once.
+  const int c_off = (int)blockIdx.x % nc;
+  auto issue = [&](u32x4_t *xa, u32x4_t *rb, int c) {
+    const int cc = c + c_off < nc ? c + c_off : c + c_off - nc;
+    const int ko = cc * kRouterK;
+    if (wv == 0) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        a[B][q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_x, xo, so + q * 32, 0));
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds(xrow[i] + ko, (__attribute__((address_space(3))) void *)(xa + 64 * i), 16, 0,
+                                         0);
+    }
 #pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        // rows past E: clamped to row E - 1 (their results are not stored)
-        const uint32_t o = e0 + 32 * j + r < E ? ro + (uint32_t)(32 * j * K * 2) : (uint32_t)(E - 1) * (K * 2) + k0 + h * 16;
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds(rrow[i] + ko,
+                                       (__attribute__((address_space(3))) void *)(rb + 64 * (8 * wv + i)), 16, 0, 0);
+  };
+  typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+  f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  auto mma_chunk = [&](const u32x4_t *xa, const u32x4_t *rb) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          b[B][j][q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_r, o, so + q * 32, 0));
+    for (int s = 0; s < kRouterK / 32; ++s) {
+      const int c = 4 * s + (lane >> 4);
+      const u32x4_t av = xa[rt_pos(lane & 15, c)];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const u32x4_t bv = rb[rt_pos(32 * wv + 16 * j + (lane & 15), c)];
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                         __builtin_bit_cast(bf16x8_t, bv), acc[j], 0, 0, 0);
       }
-    };
-    auto mma = [&](auto buf_c) {
-      constexpr int B = decltype(buf_c)::value;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b[B][j][q]),
-                                                           __builtin_bit_cast(bf16x8_t, a[B][q]), acc[j], 0, 0, 0);
-    };
-    // (scheduling barriers keep each chunk's loads ahead of the MFMAs of
-    // the chunk before it)
-    load(IC<0>{}, 0);
-    for (int kc = 0; kc < nk; kc += 2) {
-      load(IC<1>{}, kc + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      mma(IC<0>{});
-      __builtin_amdgcn_sched_barrier(0);
-      load(IC<0>{}, kc + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      mma(IC<1>{});
-    }
-    if (wv > 0) {
-#pragma unroll
-      for (int j = 0; j < NT; ++j) part[wv - 1][j][lane] = acc[j];
-    }
-    __syncthreads();
-    if (wv > 0) return;
-#pragma unroll
-    for (int w = 0; w < 3; ++w)
-#pragma unroll
-      for (int j = 0; j < NT; ++j) acc[j] += part[w][j][lane];
-    // acc[j][i]: expert e0 + 32 j + 8 (i / 4) + 4 h + i % 4, token t0 + r
-    const int t = t0 + r;
-    if (t < M) {
-#pragma unroll
-      for (int j = 0; j < NT; ++j)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int c = e0 + 32 * j + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (c < E) logits[(size_t)t * E + c] = (uint16_t)f32_to_bf16(acc[j][i]);
-        }
     }
   };
-  (void)nte;  // every block holds one 32-expert tile (rows past E are clamped)
-  run(IC<kRouterExperts / 32>{});
+  auto bufs = [&](auto j_c, auto &&f) {
+    constexpr int J = decltype(j_c)::value;
+    if constexpr (J == 0) f(xa0, rb0);
+    else if constexpr (J == 1) f(xa1, rb1);
+    else if constexpr (J == 2) f(xa2, rb2);
+    else f(xa3, rb3);
+  };
+  // Chunk c lives in buffer c % 4.  Every chunk step issues one chunk's
+  // loads (past the end: the last chunk again, into a buffer no longer
+  // read), so the count of loads issued after chunk c + 1's is always two
+  // chunks' worth: wave 0 moves 12 per chunk, the others 8.  The barrier
+  // after chunk c waits for chunk c + 1 and for every wave's reads of c.
+  auto barrier = [&]() {
+    asm volatile("" ::: "memory");
+    if (wv == 0) __builtin_amdgcn_s_waitcnt(0x4078);  // vmcnt(24) lgkmcnt(0)
+    else __builtin_amdgcn_s_waitcnt(0x4070);           // vmcnt(16) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  bufs(IC<0>{}, [&](u32x4_t *xa, u32x4_t *rb) { issue(xa, rb, 0); });
+  bufs(IC<1>{}, [&](u32x4_t *xa, u32x4_t *rb) { issue(xa, rb, min(1, nc - 1)); });
+  bufs(IC<2>{}, [&](u32x4_t *xa, u32x4_t *rb) { issue(xa, rb, min(2, nc - 1)); });
+  barrier();  // chunk 0 (two chunks issued after it)
+  auto step = [&](auto j_c, int c) {
+    constexpr int J = decltype(j_c)::value;
+    bufs(IC<(J + 3) % 4>{}, [&](u32x4_t *xa, u32x4_t *rb) { issue(xa, rb, min(c + 3, nc - 1)); });
+    bufs(j_c, [&](u32x4_t *xa, u32x4_t *rb) { mma_chunk(xa, rb); });
+    barrier();
+  };
+  for (int c = 0; c < nc; c += 4) {
+    step(IC<0>{}, c);
+    if (c + 1 >= nc) break;
+    step(IC<1>{}, c + 1);
+    if (c + 2 >= nc) break;
+    step(IC<2>{}, c + 2);
+    if (c + 3 >= nc) break;
+    step(IC<3>{}, c + 3);
+  }
+  // acc[j][i]: token t0 + 4 (lane / 16) + i, expert e0 + 32 w + 16 j + lane % 16
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int e = e0 + 32 * wv + 16 * j + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 4 * (lane >> 4) + i;
+      if (t < M && e < E) logits[(size_t)t * E + e] = (uint16_t)f32_to_bf16(acc[j][i]);
+    }
+  }
 }
 
 // Router logits of decode-size batches: logits[t, c] = bf16(fp32 x[t] . R[c])
