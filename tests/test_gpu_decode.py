@@ -198,6 +198,29 @@ def test_forced_routing_and_determinism():
     assert np.array_equal(rf["out"], out_c)
 
 
+def test_forced_routing_dropped_ids():
+    _say("decode forced routing with dropped ids, and with every id dropped")
+    inp = synth.make_small(403, M=5, H=256, E=16, I=128, SI=128, top_k=4, router_std=0.3)
+    ref = oracle.moe_block(inp)
+    ids = np.array(ref["ids"], dtype=np.int32).reshape(5, 4)
+    tw = np.array(ref["tw"], dtype=np.float32).reshape(5, 4)
+    ids[0, 1] = -1
+    ids[2, 3] = 16      # past E: dropped as well
+    ids[4, :] = -1      # a token with no routed pair at all
+    rf = G.run_block(fm, inp, "decode", forced=(ids, tw))
+    keep = ((ids >= 0) & (ids < 16)).reshape(-1)
+    y = rf["y"].copy()
+    y[~keep] = 0        # rows of dropped pairs are not written
+    tw0 = np.where(keep, tw.reshape(-1), 0.0).astype(np.float32)
+    out_c, _ = oracle.combine(y, tw0, rf["sh"], 4)
+    assert np.array_equal(rf["out"], out_c)
+    # every id dropped: no routed pair in the call, the output is the shared
+    # expert's (bf16(0) + sh)
+    ra = G.run_block(fm, inp, "decode", forced=(np.full_like(ids, -1), tw))
+    assert np.array_equal(ra["out"], ra["sh"])
+    assert np.array_equal(ra["sh"], rf["sh"])  # the shared expert does not depend on the routing
+
+
 def test_decode_edge_cases():
     _say("decode edge cases: M=0, top_k=E, E=1")
     # M = 0: valid no-op
