@@ -43,7 +43,7 @@ Workspace carve_workspace(void *base, int M, int H, int E, int I, int SI, int to
   w.sync = static_cast<DecodeSync *>(take(sizeof(DecodeSync)));
   w.route_counters = static_cast<int32_t *>(take(sizeof(int32_t) * kRouteCounterWords));
   w.logits = static_cast<uint16_t *>(take(2 * (size_t)M * E));
-  w.tlog = static_cast<unsigned long long *>(take(8 * (size_t)M * E));
+  w.tlog = static_cast<unsigned long long *>(take(8 * (size_t)kFlagCopies * M * E));
   w.ids = static_cast<int32_t *>(take(4 * P));
   w.tw = static_cast<float *>(take(4 * P));
   w.plan.n_active = static_cast<int32_t *>(take(16));

@@ -104,7 +104,7 @@ struct Params {
   const int32_t *ids_in; // forced routing (NULL = route)
   const float *tw_in;
   uint16_t *logits;
-  unsigned long long *tlog;  // [M, E] (seq << 32) | bf16 bits of the logit
+  unsigned long long *tlog;  // [kFlagCopies][M, E] (seq << 32) | bf16 bits of the logit
   int32_t *ids;
   float *tw;
   uint16_t *act;
@@ -297,7 +297,7 @@ __device__ __forceinline__ int owner(const Route &R, const int *cum, int s, int 
 __device__ void topk_token(const Params &P, int t, Route &R, int *scratch) {
   const int lane = lane_id();
   const int E = P.E, k = P.top_k;
-  const unsigned long long *trow = P.tlog + (size_t)t * E;
+  const unsigned long long *trow = P.tlog + ((size_t)(blockIdx.x % kFlagCopies) * P.M + t) * E;
   // four slots per lane, expert lane + 64 i; slots past E read expert E - 1
   // and are masked, so every load is issued at once and nothing branches
   int ee[4];
@@ -399,7 +399,7 @@ __device__ void topk_token(const Params &P, int t, Route &R, int *scratch) {
 __device__ void topk_token_long(const Params &P, int t, Route &R) {
   const int lane = lane_id();
   const int E = P.E, k = P.top_k;
-  const unsigned long long *trow = P.tlog + (size_t)t * E;
+  const unsigned long long *trow = P.tlog + ((size_t)(blockIdx.x % kFlagCopies) * P.M + t) * E;
   unsigned long long v[4] = {0ull, 0ull, 0ull, 0ull};
   bool done = false;
   for (int it = 0, nap = 1; it < P.polls; ++it) {
@@ -694,8 +694,10 @@ __device__ void route_item(const Params &P, int r, const uint16_t *xl, WaitX &&w
         acc = dot2_bf16(w[i][3], xv[ti][i][3], acc);
       }
       acc = group_sum<kWave>(acc);
-      if (lane == kWave - 1 && g + ti < nt)
-        st_dev(&P.tlog[(size_t)(t0 + g + ti) * P.E + e], tag | f32_to_bf16(acc));
+      // one copy per XCD (every block polls the logits)
+      acc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, acc), kWave - 1));
+      if (lane < kFlagCopies && g + ti < nt)
+        st_dev(&P.tlog[((size_t)lane * P.M + t0 + g + ti) * P.E + e], tag | f32_to_bf16(acc));
     }
   }
 }
@@ -819,6 +821,14 @@ __device__ __forceinline__ void block_done(int *ctr, int *flag, int seq) {
   stores_performed();
   if (lane_id() == 0) {
     if (atomicAdd(ctr, 1) == kWaves - 1) st_dev(flag, seq);
+  }
+}
+// The same with the flag written to every copy flag[c * stride], c < kFlagCopies.
+__device__ __forceinline__ void block_done_copies(int *ctr, int *flag, int stride, int seq) {
+  stores_performed();
+  if (lane_id() == 0) {
+    if (atomicAdd(ctr, 1) == kWaves - 1)
+      for (int c = 0; c < kFlagCopies; ++c) st_dev(flag + c * stride, seq);
   }
 }
 
@@ -951,7 +961,7 @@ decode_kernel(Params P) {
       }
       TRACE(P, 11);
     }
-    block_done(&R.done_sg, &S->sg[blockIdx.x], P.seq);
+    block_done_copies(&R.done_sg, &S->sg[0][blockIdx.x], kMaxSharedBlocks, P.seq);
   }
 
   // ---- phase A3: shared down, one item (RW rows) per wave (item j: block
@@ -982,7 +992,8 @@ decode_kernel(Params P) {
         // the block's first shared down wave polls the flags, the others
         // wait for its word in LDS
         if (ws == 0) {
-          wave_wait_flags(S->sg, sh0, sh0 + min(nbs, P.n_sgu), P.seq, P.polls, S, kWaitSharedGateUp);
+          wave_wait_flags(S->sg[blockIdx.x % kFlagCopies], sh0, sh0 + min(nbs, P.n_sgu), P.seq, P.polls, S,
+                          kWaitSharedGateUp);
           if (lane == 0) __hip_atomic_store(&R.sg_ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         } else {
           wait_lds_at_least(&R.sg_ready, 1, S);
@@ -1120,7 +1131,7 @@ decode_kernel(Params P) {
     int last = 0;
     if (lane == 0) last = atomicAdd(&R.done_b, 1) == kWaves - 1;
     if (__builtin_amdgcn_readfirstlane(last)) {
-      if (lane == 0) st_dev(&S->gb[blockIdx.x], P.seq);
+      if (lane < kFlagCopies) st_dev(&S->gb[lane][blockIdx.x], P.seq);
       double *sums = reinterpret_cast<double *>(xs);
       const int nsum = n_rg * P.M * Gm::DN::RW;
       for (int i = lane; i < nsum; i += kWave) sums[i] = 0.0;
@@ -1240,7 +1251,7 @@ decode_kernel(Params P) {
       const int nx = np - nc < kCacheX ? np - nc : kCacheX;
       if (!st.act) {
         if (__hip_atomic_load(&R.slot_ready[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) {
-          wave_wait_flags(S->gb, owner_block(R, R.cum_gu, s, 0, QB, P.nb),
+          wave_wait_flags(S->gb[blockIdx.x % kFlagCopies], owner_block(R, R.cum_gu, s, 0, QB, P.nb),
                           owner_block(R, R.cum_gu, s, Gm::N_GU - 1, QB, P.nb) + 1, P.seq, P.polls, S,
                           kWaitGateUp);
           if (lane == 0)

@@ -27,10 +27,15 @@ constexpr int kMaxSharedBlocks = 1024;
 // Completion flags of the decode kernel.  A flag holds the sequence number
 // of the call that set it (every call gets a new one), so flags never need
 // resetting.
+// Copies of a flag that many blocks poll: a reader polls the copy of its
+// own XCD (block id mod 8), so each copy's lines are polled by an eighth of
+// the grid instead of all of it.
+constexpr int kFlagCopies = 8;
+
 struct DecodeSync {
-  int sg[kMaxSharedBlocks];  // shared gate/up block done
+  int sg[kFlagCopies][kMaxSharedBlocks];  // shared gate/up block done (one copy per XCD)
   int sd[kMaxSharedBlocks];  // shared down block done
-  int gb[kMaxDecodeBlocks];  // the block's routed gate/up items done
+  int gb[kFlagCopies][kMaxDecodeBlocks];  // the block's routed gate/up items done (one copy per XCD)
   int db[kMaxDecodeBlocks];  // (unused: kept so the workspace layout does not change)
   int wait_err;              // OR of the kinds of waits that gave up (0 = none)
   int probe;                 // never written: the target of the test hook's wait
@@ -61,7 +66,7 @@ struct DecodeArgs {
   const int32_t *ids_in;        // forced routing, NULL = route
   const float *tw_in;
   uint16_t *logits;
-  unsigned long long *tlog;     // [M, E] logits tagged with the call's sequence number
+  unsigned long long *tlog;     // [kFlagCopies][M, E] logits tagged with the call's sequence number
   int32_t *ids;
   float *tw;
   uint16_t *act, *y, *sact, *sh, *out;
@@ -89,7 +94,7 @@ struct Workspace {
   DecodeSync *sync;         // zero between calls
   int32_t *route_counters;  // [kRouteCounterWords], zero between calls
   uint16_t *logits;    // [M, E]
-  unsigned long long *tlog;  // [M, E] decode: tagged logits
+  unsigned long long *tlog;  // [kFlagCopies][M, E] decode: tagged logits (one copy per XCD)
   int32_t *ids;        // [M, k]
   float *tw;           // [M, k]
   Plan plan;
