@@ -231,7 +231,7 @@ int flint_moe_decode(const uint16_t *x, const uint16_t *router,
  * device memory (serving loops that must not call hipMalloc, harnesses that
  * forbid it).  Same arguments (minus ws), rule, limits and errors as
  * flint_moe_decode; no memory is allocated or freed.  Its scratch is a
- * 4 MiB array inside the library, one per GPU, kept until the process
+ * 5 MiB array inside the library, one per GPU, kept until the process
  * ends; sizes whose workspace would exceed it (flint_moe_workspace_bytes)
  * return FLINT_ERR_WORKSPACE (every size the decode entry points accept
  * fits).  Past 16 tokens the shared expert runs on `stream` itself (no

@@ -70,8 +70,9 @@ Workspace carve_workspace(void *base, int M, int H, int E, int I, int SI, int to
 // hipGetSymbolAddress (with that device current) and only that address is
 // passed to kernels.  kScratchBytes covers the largest decode workspace the
 // decode entry points accept (M <= 64, M * top_k <= 512, E <= 256, H <= 2048,
-// I = SI <= 768: about 3.4 MiB).
-constexpr size_t kScratchBytes = size_t(4) << 20;
+// I = SI <= 768: 4.28 MiB at M = 64, top_k = 8, E = 256, of which y is
+// 2 MiB and the eight copies of the tagged logits 1 MiB).
+constexpr size_t kScratchBytes = size_t(5) << 20;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 constexpr int kMaxScratchDevices = 64;

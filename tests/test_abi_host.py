@@ -47,6 +47,14 @@ def test_workspace_bytes():
         fm.flint_moe_workspace_bytes(8, 2048, 8, 768, 768, 9)    # top_k > E
 
 
+def test_decode_workspaces_fit_the_noalloc_scratch():
+    # flint_moe_decode_noalloc's scratch (5 MiB, include/flint_moe.h) holds
+    # the workspace of every size the decode entry points accept; the
+    # largest are at M * top_k = 512 with E = 256.
+    for M, k in ((64, 8), (32, 16), (16, 32), (8, 64)):
+        assert fm.flint_moe_workspace_bytes(M, 2048, 256, 768, 768, k) <= 5 << 20, (M, k)
+
+
 # Fake, never-dereferenced device addresses: every case below must be
 # rejected by host validation before anything is queued.
 A = ctypes.c_void_p(0x10000)

@@ -39,7 +39,9 @@ def _debug(M, E, k, I, H, SI):
 
 
 def test_noalloc_matches_decode_on_two_calls():
-    cases = [synth.make_small(989, M=40, H=512, E=16, I=256, SI=256, top_k=4, router_std=0.3),
+    cases = [# the largest decode workspace (M * top_k = 512, E = 256: 4.28 MiB of the 5 MiB)
+             synth.make_small(991, M=64, H=2048, E=256, I=768, SI=768, top_k=8, router_std=0.3),
+             synth.make_small(989, M=40, H=512, E=16, I=256, SI=256, top_k=4, router_std=0.3),
              # (M > 16: the grouped chain on the skinny GEMMs, shared expert inline)
              synth.make_inputs(1),  # M = 8, E = 128, H = 2048, I = 768, k = 8
              synth.make_small(990, M=3, H=2048, E=32, I=768, SI=768, top_k=4, router_std=0.3)]
