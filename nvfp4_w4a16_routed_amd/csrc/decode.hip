@@ -294,28 +294,30 @@ __device__ __forceinline__ int owner(const Route &R, const int *cum, int s, int 
 // selected keys are then ranked among themselves (descending key = the
 // selection order), which fixes the order of ids, of the weights and of the
 // fp32 sum of the scores.
+// NS slots per lane (E <= 64 NS): expert lane + 64 i in slot i.
+template <int NS>
 __device__ void topk_token(const Params &P, int t, Route &R, int *scratch) {
   const int lane = lane_id();
   const int E = P.E, k = P.top_k;
   const unsigned long long *trow = P.tlog + ((size_t)(blockIdx.x % kFlagCopies) * P.M + t) * E;
-  // four slots per lane, expert lane + 64 i; slots past E read expert E - 1
-  // and are masked, so every load is issued at once and nothing branches
-  int ee[4];
-  bool valid[4];
+  // slots past E read expert E - 1 and are masked, so every load is issued
+  // at once and nothing branches
+  int ee[NS];
+  bool valid[NS];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NS; ++i) {
     ee[i] = lane + kWave * i;
     valid[i] = ee[i] < E;
     ee[i] = valid[i] ? ee[i] : E - 1;
   }
-  unsigned long long v[4];
+  unsigned long long v[NS];
   bool done = false;
   for (int it = 0, nap = 1; it < P.polls; ++it) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = ld_dev(&trow[ee[i]]);
+    for (int i = 0; i < NS; ++i) v[i] = ld_dev(&trow[ee[i]]);
     bool ok = true;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ok &= !valid[i] || (uint32_t)(v[i] >> 32) == (uint32_t)P.seq;
+    for (int i = 0; i < NS; ++i) ok &= !valid[i] || (uint32_t)(v[i] >> 32) == (uint32_t)P.seq;
     if (__all(ok)) {
       done = true;
       break;
@@ -325,15 +327,15 @@ __device__ void topk_token(const Params &P, int t, Route &R, int *scratch) {
   }
   if (!done) wait_failed(P.sync, kWaitLogits);
   TRACE(P, 13);
-  int keys[4];
+  int keys[NS];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NS; ++i) {
     const uint32_t bits = (uint32_t)v[i] & 0xffffu;
     keys[i] = valid[i] ? rank_key(bits, ee[i]) : kNoKey;
   }
   if (blockIdx.x == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NS; ++i)
       if (valid[i]) P.logits[(size_t)t * E + ee[i]] = (uint16_t)(v[i] & 0xffffu);
   }
   // Lanes j < top_k (top_k <= 64 here) get the selected keys, lane j the
@@ -343,29 +345,33 @@ __device__ void topk_token(const Params &P, int t, Route &R, int *scratch) {
     // k rounds of a wave maximum (keys are unique): the short dependent
     // chain of a small top_k
     for (int r = 0; r < k; ++r) {
-      const int m = wave_max_i32(max(max(keys[0], keys[1]), max(keys[2], keys[3])));
+      int lm = keys[0];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) keys[i] = keys[i] == m ? kNoKey : keys[i];
+      for (int i = 1; i < NS; ++i) lm = max(lm, keys[i]);
+      const int m = wave_max_i32(lm);
+#pragma unroll
+      for (int i = 0; i < NS; ++i) keys[i] = keys[i] == m ? kNoKey : keys[i];
       key = lane == r ? m : key;
     }
   } else {
     // the top_k-th largest key, by a radix search from the top bit with
     // ballot counts over the keys offset to [0, 2^24) (no key: -1)
-    int ukey[4];
+    int ukey[NS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ukey[i] = keys[i] == kNoKey ? -1 : keys[i] + (1 << 23);
+    for (int i = 0; i < NS; ++i) ukey[i] = keys[i] == kNoKey ? -1 : keys[i] + (1 << 23);
     int thr = 0;
 #pragma unroll
     for (int bit = 23; bit >= 0; --bit) {
       const int cand = thr | (1 << bit);
-      const int cnt = __popcll(__ballot(ukey[0] >= cand)) + __popcll(__ballot(ukey[1] >= cand)) +
-                      __popcll(__ballot(ukey[2] >= cand)) + __popcll(__ballot(ukey[3] >= cand));
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < NS; ++i) cnt += __popcll(__ballot(ukey[i] >= cand));
       thr = cnt >= k ? cand : thr;
     }
     // compact the selected keys into scratch[0 .. k), then rank them
     int base = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NS; ++i) {
       const bool sel = ukey[i] >= thr;
       const unsigned long long m = __ballot(sel);
       if (sel) scratch[base + __popcll(m & ((1ull << lane) - 1ull))] = keys[i];
@@ -1038,7 +1044,9 @@ decode_kernel(Params P) {
           if ((unsigned)e < (unsigned)P.E) atomicOr(&R.tokmask[e], 1ull << t);  // bad ids dropped
         }
       } else if (k <= kWave) {
-        topk_token(P, t, R, reinterpret_cast<int *>(slice));
+        if (P.E <= kWave) topk_token<1>(P, t, R, reinterpret_cast<int *>(slice));
+        else if (P.E <= 2 * kWave) topk_token<2>(P, t, R, reinterpret_cast<int *>(slice));
+        else topk_token<4>(P, t, R, reinterpret_cast<int *>(slice));
       } else {
         topk_token_long(P, t, R);
       }
