@@ -31,38 +31,46 @@ constexpr int kThreads = 256;  // 4 waves
 // Top-k of one token's logits by one wave (top_k <= E <= 256).  Selection j
 // is kept in a register of lane j % 64 (slot j / 64).  Writes the ids, tw
 // and (if non-NULL) scores rows of the token.
-__device__ void topk_token(const uint16_t *lrow, int E, int top_k, int32_t *ids, float *tw,
-                           float *scores) {
+// NS key slots per lane (E <= 64 NS): expert lane + 64 i in slot i.
+template <int NS>
+__device__ void topk_token_ns(const uint16_t *lrow, int E, int top_k, int32_t *ids, float *tw,
+                              float *scores) {
   const int lane = threadIdx.x & (kWave - 1);
-  int keys[4], sel[4] = {kNoKey, kNoKey, kNoKey, kNoKey};
+  int keys[NS], sel[NS];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int e = lane + kWave * i;
+  for (int i = 0; i < NS; ++i) {
+    const int e = lane + kWave * i;
     keys[i] = (e < E) ? rank_key(lrow[e], e) : kNoKey;
+    sel[i] = kNoKey;
   }
   for (int j = 0; j < top_k; ++j) {
-    int m = max(max(keys[0], keys[1]), max(keys[2], keys[3]));
-    int best = wave_max_i32(m);
+    int m = keys[0];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (keys[i] == best) keys[i] = kNoKey;
-      if ((j >> 6) == i && lane == (j & (kWave - 1))) sel[i] = best;
+    for (int i = 1; i < NS; ++i) m = max(m, keys[i]);
+    const int best = wave_max_i32(m);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      keys[i] = keys[i] == best ? kNoKey : keys[i];
+      if ((j >> 6) == i) sel[i] = lane == (j & (kWave - 1)) ? best : sel[i];
     }
   }
   // Sigmoid score of each selected logit, by the lane that holds it.
-  float s[4];
+  float s[NS];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) s[i] = kWave * i + lane < top_k ? router_score(sel[i]) : 0.0f;
+  for (int i = 0; i < NS; ++i) s[i] = kWave * i + lane < top_k ? router_score(sel[i]) : 0.0f;
   // Renormalisation: fp32 sum in selection order, then one RN division each.
   float S = 0.0f;
   for (int j = 0; j < top_k; ++j) {
     const int i = j >> 6;
-    float v = (i == 0) ? s[0] : (i == 1) ? s[1] : (i == 2) ? s[2] : s[3];
-    S = S + __shfl(v, j & (kWave - 1), kWave);
+    float v = s[0];
+#pragma unroll
+    for (int ii = 1; ii < NS; ++ii) v = i == ii ? s[ii] : v;
+    S = S + __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v),
+                                                                 j & (kWave - 1)));
   }
   const float D = S + 1e-20f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NS; ++i) {
     const int j = kWave * i + lane;
     if (j < top_k) {
       ids[j] = key_expert(sel[i]);
@@ -72,7 +80,13 @@ __device__ void topk_token(const uint16_t *lrow, int E, int top_k, int32_t *ids,
   }
 }
 
-// Inclusive scan of one int over the 256 threads of the block.
+__device__ void topk_token(const uint16_t *lrow, int E, int top_k, int32_t *ids, float *tw,
+                           float *scores) {
+  if (E <= kWave) topk_token_ns<1>(lrow, E, top_k, ids, tw, scores);
+  else if (E <= 2 * kWave) topk_token_ns<2>(lrow, E, top_k, ids, tw, scores);
+  else topk_token_ns<4>(lrow, E, top_k, ids, tw, scores);
+}
+
 __device__ int block_inclusive_scan(int v, int *lds4) {
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
 #pragma unroll
