@@ -858,10 +858,11 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint16_t *__restrict
                                                       const int32_t *__restrict__ ids,
                                                       const uint16_t *__restrict__ sh, int M, int H,
                                                       int E, int k, uint16_t *__restrict__ out) {
-  const long gid = (long)blockIdx.x * 256 + threadIdx.x;
-  const int per_row = H / 8;
-  if (gid >= (long)M * per_row) return;
-  const int t = (int)(gid / per_row), h = (int)(gid % per_row) * 8;
+  // block (t, c): token t, columns [2048 c, 2048 c + 2048); the token is the
+  // block's, so its ids and weights are scalar loads
+  const int t = blockIdx.x;
+  const int h = ((int)blockIdx.y * 256 + (int)threadIdx.x) * 8;
+  if (h >= H) return;
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int j0 = 0; j0 < k; j0 += 8) {
     u32x4_t v[8];
@@ -1266,9 +1267,9 @@ hipError_t launch_grouped(const GroupedArgs &a, hipStream_t st) {
   if (a.sh_ext && a.sh_ready && (err = hipStreamWaitEvent(st, (hipEvent_t)a.sh_ready, 0)) != hipSuccess)
     return err;
   {
-    const long n = (long)M * (H / 8);
     const uint16_t *shp = a.sh_ext ? a.sh_ext : (a.sgu ? a.sh : nullptr);
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.y, a.tw,
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)M, (unsigned)((H / 8 + 255) / 256)), dim3(256), 0, st,
+                       a.y, a.tw,
                        a.ids, shp, M, H, E, k, a.out);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
