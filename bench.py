@@ -7,7 +7,9 @@ headline workload is decode of M=8 tokens against E=128 NVFP4 experts
 (H=2048, I=768, top_k=8, shared SwiGLU expert of width 768).  Weights are
 rotated over L layer copies, L sized from the bytes one call touches, so the
 same weights are reused only after more than twice the 256 MB Infinity Cache
-has streamed: weight bytes really come from HBM.
+has streamed: weight bytes really come from HBM.  Every timing runs the
+workload untimed for --settle seconds (0.3 by default) and then the warm-up
+calls before its timed calls, so the GPU's clocks are at their loaded level.
 
 Prints one JSON line: tokens/s of the headline workload, the achieved HBM
 bandwidth over its algorithmic bytes, the roofline of its one kernel (the
