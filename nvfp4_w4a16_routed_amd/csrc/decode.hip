@@ -62,6 +62,7 @@ constexpr int kRouteTokens = 4;           // tokens per routing item (one load r
 constexpr int kXLdsBytes = kDecodeXStage;  // x staged in LDS when M * H * 2 fits
 constexpr int kSliceBytes = 4096;         // per-wave LDS slice (results, act cache)
 constexpr int kMaxRowGroups = 16;         // down row groups per block
+constexpr int kShPreMax = kMaxRowGroups * 16 * 8;  // shared output values staged for the combine
 constexpr int kCacheLdsBytes = kWaves * kSliceBytes;
 // Cache-policy operand of a direct global->LDS load that reads at device
 // scope (the SC1 bit, as the device-scope loads in common.hpp use).
@@ -243,6 +244,8 @@ struct Route {
   int slot_ready[kMaxExperts];  // phase C: the slot's gate/up blocks are done
   int done_rg[kMaxRowGroups];   // phase C: items done per row group of the block
   int sums_ready;               // phase C: the fp64 sums are zeroed
+  int sh_ready;                 // phase C: sh_pre holds the shared output of the block's rows
+  uint16_t sh_pre[kShPreMax];   // [n_rg][M][RW] shared output rows of the combine
 };
 
 // Work balance.  Item (s, j) of a phase (slot s, j < N items per slot)
@@ -872,6 +875,7 @@ decode_kernel(Params P) {
 
   if (threadIdx.x == 0) {
     R.done_sg = R.done_sd = R.topk_done = R.plan_ready = R.x_staged = R.sg_ready = R.sums_ready = 0;
+    R.sh_ready = 0;
   }
   if (threadIdx.x < kMaxExperts) {
     R.tokmask[threadIdx.x] = 0ull;
@@ -1145,6 +1149,37 @@ decode_kernel(Params P) {
       for (int i = lane; i < nsum; i += kWave) sums[i] = 0.0;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       if (lane == 0) __hip_atomic_store(&R.sums_ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      // The shared output of the block's rows, staged for the combines now
+      // (the shared expert is done long before the routed down items), so a
+      // combine waits for no round trip of its own.
+      if (P.sgu || P.sh_ext) {
+        constexpr int RWC = Gm::DN::RW;
+        for (int lr = 0; lr < n_rg; ++lr) {
+          const int h_base = ((int)blockIdx.x + lr * P.nb) * RWC;
+          if (P.sgu) {
+            // the blocks holding the shared down items of these rows
+            bool done = false;
+            const int j0 = h_base / Gm::SDN::RW, j1 = (h_base + RWC - 1) / Gm::SDN::RW;
+            for (int it = 0, nap = 1; it < P.polls; ++it) {
+              bool ok = true;
+              for (int j = j0 + lane; j <= j1; j += kWave) ok &= ld_dev(&S->sd[sh0 + j % nbs]) == P.seq;
+              if (__all(ok)) {
+                done = true;
+                break;
+              }
+              for (int z = 0; z < nap; ++z) __builtin_amdgcn_s_sleep(2);
+              nap = nap < 4 ? nap * 2 : 4;
+            }
+            if (!done) wait_failed(S, kWaitCombineShared);
+          }
+          for (int l = lane; l < P.M * RWC; l += kWave) {
+            const size_t o = (size_t)(l / RWC) * H + h_base + l % RWC;
+            R.sh_pre[lr * P.M * RWC + l] = P.sgu ? ld_dev(&P.sh[o]) : P.sh_ext[o];
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        if (lane == 0) __hip_atomic_store(&R.sh_ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
     }
   }
   TRACE(P, 4);
@@ -1208,28 +1243,14 @@ decode_kernel(Params P) {
     auto combine = [&](int lr, int h_base) {
       const double *gs = sums + (size_t)lr * P.M * RW;
       TRACE(P, 6);
-      if (P.sgu) {
-        // the blocks holding the shared down items of these rows (done long
-        // before the routed ones)
-        bool done = false;
-        const int j0 = h_base / Gm::SDN::RW, j1 = (h_base + RW - 1) / Gm::SDN::RW;
-        for (int it = 0, nap = 1; it < P.polls; ++it) {
-          bool ok = true;
-          for (int j = j0 + lane; j <= j1; j += kWave) ok &= ld_dev(&S->sd[sh0 + j % nbs]) == P.seq;
-          if (__all(ok)) {
-            done = true;
-            break;
-          }
-          for (int z = 0; z < nap; ++z) __builtin_amdgcn_s_sleep(2);
-          nap = nap < 4 ? nap * 2 : 4;
-        }
-        if (!done) wait_failed(S, kWaitCombineShared);
-      }
+      const bool has_sh = P.sgu || P.sh_ext;
+      if (has_sh) wait_lds_at_least(&R.sh_ready, 1, S);
+      const uint16_t *shp = R.sh_pre + (size_t)lr * P.M * RW;
       for (int l = lane; l < P.M * RW; l += kWave) {
         const int t = l / RW, r = l % RW;
         const float routed = round_bf16((float)gs[t * RW + r]);
         const size_t o = (size_t)t * H + h_base + r;
-        const float sv = P.sgu ? bf16_to_f32(ld_dev(&P.sh[o])) : P.sh_ext ? bf16_to_f32(P.sh_ext[o]) : 0.0f;
+        const float sv = has_sh ? bf16_to_f32(shp[l]) : 0.0f;
         P.out[o] = (uint16_t)f32_to_bf16(routed + sv);
       }
     };
@@ -1377,7 +1398,8 @@ hipError_t launch(Params P, hipStream_t st) {
   P.nb = gi.nb;
   // the down row groups of a block and their fp64 sums (in the staging area)
   const int n_rg = (Gm::N_DN + P.nb - 1) / P.nb;
-  if (n_rg > kMaxRowGroups || (size_t)n_rg * P.M * Gm::DN::RW * 8 > kXLdsBytes / 2)
+  if (n_rg > kMaxRowGroups || (size_t)n_rg * P.M * Gm::DN::RW * 8 > kXLdsBytes / 2 ||
+      n_rg * P.M * Gm::DN::RW > kShPreMax)
     return hipErrorInvalidValue;
   const int nTG = (P.M + kRouteTokens - 1) / kRouteTokens;
   P.n_route = P.ids_in ? 0 : P.E * nTG;  // routing items (expert, token group)
